@@ -1,0 +1,206 @@
+"""CPU oracle for the SimSD verification path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package. The product path (the HIP library and its binding)
+never does, and the two share no code.
+
+The arithmetic lives in ``simsd_oracle.c`` (plain C, fp64 attention and RoPE,
+fp32 accept/reject decisions); this module only marshals numpy arrays into it.
+Every function cites the page section it follows in the C source.
+
+Parity status of each function (what pins it, all in ``tests/test_oracle_*``):
+  allowed / mask_matrix   pinned: hand-derived mask fixture, counting and
+                          permutation invariants.
+  verify_attention        pinned: library attention on explicitly gathered keys,
+                          closed forms, perturbation and permutation invariance.
+                          The rule for data-token rows is this build's reading
+                          (the pages define only mask-slot rows): pinned only
+                          to that stated reading.
+  rope_copy               pinned: complex-number form, closed forms, relative-
+                          position property, the copy rule.
+  accept                  pinned: vocabulary-4 enumeration of acceptance and
+                          residual laws, the lossless identity, special cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "simsd_oracle.c")
+LIB = os.path.join(HERE, "libsimsd_oracle.so")
+
+DATA_CAUSAL, DATA_BIDIR, DATA_SKIP = 0, 1, 2
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.c_double
+        lib.simsd_oracle_tau_inverse.argtypes = [P, I, P]
+        lib.simsd_oracle_tau_inverse.restype = I
+        lib.simsd_oracle_allowed.argtypes = [I, P, I, I, I]
+        lib.simsd_oracle_allowed.restype = I
+        lib.simsd_oracle_attention_row.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, D, I, P, P]
+        lib.simsd_oracle_attention_row.restype = None
+        lib.simsd_oracle_verify_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, D, I, P, P]
+        lib.simsd_oracle_verify_attention.restype = I
+        lib.simsd_oracle_rope_copy.argtypes = [P, P, I, I, I, I, D, I, I]
+        lib.simsd_oracle_rope_copy.restype = None
+        lib.simsd_oracle_accept.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P]
+        lib.simsd_oracle_accept.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float64)
+    return np.ascontiguousarray(a)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def tau_inverse(tau):
+    """Return (inv, ok): inv[t-1] = 0-based position with label t."""
+    t = _i32(tau)
+    inv = np.empty(t.shape[0], dtype=np.int32)
+    bad = _load().simsd_oracle_tau_inverse(_p(t), t.shape[0], _p(inv))
+    return inv, bad == 0
+
+
+def allowed(B: int, tau, data_rule: int, qr: int, kr: int) -> bool:
+    t = _i32(tau)
+    return bool(_load().simsd_oracle_allowed(B, _p(t), data_rule, qr, kr))
+
+
+def mask_matrix(tau, data_rule: int = DATA_CAUSAL) -> np.ndarray:
+    """[2B][2B] boolean block mask (row = query block row, col = key block row)."""
+    t = _i32(tau)
+    B = t.shape[0]
+    lib = _load()
+    m = np.zeros((2 * B, 2 * B), dtype=bool)
+    for i in range(2 * B):
+        for j in range(2 * B):
+            m[i, j] = bool(lib.simsd_oracle_allowed(B, _p(t), data_rule, i, j))
+    return m
+
+
+def attention_row(q_row, k_pre_s, v_pre_s, k_blk_s, v_blk_s, tau_s, g: int, qr: int,
+                  scale: float | None = None, data_rule: int = DATA_CAUSAL):
+    """One query row. k_pre_s/v_pre_s [P][Hkv][d], k_blk_s/v_blk_s [2B][Hkv][d]."""
+    q = _f64(q_row)
+    kp, vp, kb, vb = _f64(k_pre_s), _f64(v_pre_s), _f64(k_blk_s), _f64(v_blk_s)
+    t = _i32(tau_s)
+    d = q.shape[0]
+    Hkv = kb.shape[1]
+    B = t.shape[0]
+    P = kp.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.empty(d, dtype=np.float64)
+    lse = np.empty(1, dtype=np.float64)
+    _load().simsd_oracle_attention_row(_p(q), _p(kp), _p(vp), P, _p(kb), _p(vb), _p(t), B, Hkv, d,
+                                       g, qr, float(scale), data_rule, _p(out), _p(lse))
+    return out, float(lse[0])
+
+
+def verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau,
+                     scale: float | None = None, data_rule: int = DATA_CAUSAL,
+                     threads: int = 1):
+    """Whole-batch verify attention. Returns (out [b][2B][Hq][d], lse [b][2B][Hq]) in fp64.
+
+    Rows skipped under DATA_SKIP are left as NaN. ``threads`` > 1 runs
+    sequences concurrently (the C call releases the GIL); results do not depend
+    on it.
+    """
+    q, kb, vb = _f64(q_blk), _f64(k_blk), _f64(v_blk)
+    kp, vp = _f64(k_pre), _f64(v_pre)
+    off = _i32(prefix_offsets)
+    t = _i32(tau)
+    b, twoB, Hq, d = q.shape
+    Hkv = kb.shape[2]
+    B = twoB // 2
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full(q.shape, np.nan)
+    lse = np.full((b, twoB, Hq), np.nan)
+    lib = _load()
+
+    def one(s):
+        o0 = int(off[s])
+        P = int(off[s + 1]) - o0
+        offs = np.array([0, P], dtype=np.int32)
+        kps = np.ascontiguousarray(kp[o0:o0 + P])
+        vps = np.ascontiguousarray(vp[o0:o0 + P])
+        os_ = np.ascontiguousarray(out[s:s + 1])
+        ls_ = np.ascontiguousarray(lse[s:s + 1])
+        bad = lib.simsd_oracle_verify_attention(
+            _p(np.ascontiguousarray(q[s:s + 1])), _p(np.ascontiguousarray(kb[s:s + 1])),
+            _p(np.ascontiguousarray(vb[s:s + 1])), _p(kps), _p(vps), _p(offs),
+            _p(np.ascontiguousarray(t[s:s + 1])), 1, B, Hq, Hkv, d, float(scale), data_rule,
+            _p(os_), _p(ls_))
+        out[s] = os_[0]
+        lse[s] = ls_[0]
+        return bad
+
+    if threads > 1 and b > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(b)))
+    else:
+        for s in range(b):
+            one(s)
+    return out, lse
+
+
+def rope_copy(x, start_pos, base: float = 10000.0, interleaved: bool = False,
+              no_copy: bool = False) -> np.ndarray:
+    """Rotated copy of x [b][2B][H][d] (fp64)."""
+    y = _f64(x).copy()
+    sp = _i32(start_pos)
+    b, twoB, H, d = y.shape
+    _load().simsd_oracle_rope_copy(_p(y), _p(sp), b, twoB // 2, H, d, float(base),
+                                   int(bool(interleaved)), int(bool(no_copy)))
+    return y
+
+
+def accept(p, q, draft, tau, u):
+    """Rejection-sampling acceptance. Returns dict of int32 arrays [b]:
+    accept_len, correction, status, boundary."""
+    pp, qq = _f32(p), _f32(q)
+    dr, t, uu = _i32(draft), _i32(tau), _f32(u)
+    b, B, V = pp.shape
+    out = {k: np.zeros(b, dtype=np.int32) for k in ("accept_len", "correction", "status", "boundary")}
+    _load().simsd_oracle_accept(_p(pp), _p(qq), _p(dr), _p(t), _p(uu), b, B, V,
+                                _p(out["accept_len"]), _p(out["correction"]), _p(out["status"]),
+                                _p(out["boundary"]))
+    return out
