@@ -1,0 +1,247 @@
+"""Benchmark of the SimSD verification hot path on one MI355X.
+
+One step = RoPE-copy -> verify attention -> acceptance over one batch of the
+headline workload (16 sequences, 32/8 heads, head_dim 128, prefix 4096, B=8,
+bf16 Q/K/V, vocab 32768), all launched on one stream with inputs resident in
+HBM. Several input sets are rotated so the 268 MB prefix KV of a step is not
+served from the 256 MB MALL.
+
+Prints one JSON line: verified blocks/s (one block = one sequence's paired
+2B block through one attention layer plus acceptance), the attention kernel's
+HBM roofline figures (HIP events around every attention launch of the timed
+steps) and the CPU oracle's throughput on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+WORKLOAD = "b8"
+METRIC = "verified blocks/s + achieved HBM GB/s & MFMA % (B=8, 4K prefix, bf16)"
+ATTN_SOURCES = ("masked_attention_simsd_amd/csrc/verify_attention.hip",
+                "masked_attention_simsd_amd/csrc/simsd_internal.h")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "verify_attention_b8_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_bytes_flops(w, lens):
+    """Algorithmic bytes and flops of verify attention for prefix lengths `lens`:
+    per sequence, bytes = K+V prefix (4 d Hkv P) + Q and O (bf16) + block K+V
+    (8 B d (Hq + Hkv)) + tau and offset (4B + 4); flops = 4 d Hq (2B P + B^2 +
+    B(B+1)/2) (mask slots see P + B keys, causal data rows P + tau(i))."""
+    d, Hq, Hkv, B = w.d, w.Hq, w.Hkv, w.B
+    nbytes = sum(4 * d * Hkv * P + 8 * B * d * (Hq + Hkv) + 4 * B + 4 for P in lens)
+    flops = sum(4 * d * Hq * (2 * B * P + B * B + B * (B + 1) // 2) for P in lens)
+    return nbytes, flops
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTER_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != attn_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, threads):
+    """The oracle chain (RoPE-copy, attention, acceptance) on the whole batch,
+    repeated for about 10 s; returns (blocks/s, reps, seconds, result of the
+    first rep for the parity check)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    w = x["workload"]
+    f64 = lambda t: t.to(torch.float64).numpy()
+    sp = x["start_pos"].numpy()
+    first, reps, t0 = None, 0, time.perf_counter()
+    while True:
+        q_r = oracle.rope_copy(f64(x["q_blk"]), sp, w.rope_base)
+        k_r = oracle.rope_copy(f64(x["k_blk"]), sp, w.rope_base)
+        # the boundary stores the rotation as bf16
+        q_r = torch.from_numpy(q_r).to(torch.bfloat16).to(torch.float64).numpy()
+        k_r = torch.from_numpy(k_r).to(torch.bfloat16).to(torch.float64).numpy()
+        out, _ = oracle.verify_attention(q_r, k_r, f64(x["v_blk"]), f64(x["k_pre"]), f64(x["v_pre"]),
+                                         x["prefix_offsets"].numpy(), x["tau"].numpy(),
+                                         threads=threads)
+        acc = oracle.accept(x["p"].numpy(), x["q"].numpy(), x["draft"].numpy(), x["tau"].numpy(),
+                            x["u"].numpy())
+        reps += 1
+        if first is None:
+            first = (out, acc)
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 20:
+            break
+    return w.b * reps / el, reps, el, first
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from masked_attention_simsd_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    binding.load_library()  # fails loudly if libsimsd.so is missing
+    dev = torch.device("cuda:0")
+    x = synth.make_inputs(WORKLOAD)
+    w = x["workload"]
+    lens = x["prefix_lens"].tolist()
+    max_prefix = max(lens)
+    log(f"workload {WORKLOAD}: {w.describe()}")
+
+    base = {k: v.to(dev) for k, v in x.items() if torch.is_tensor(v)}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.sets - 1)]
+    b, B, Hq, Hkv, d = w.b, w.B, w.Hq, w.Hkv, w.d
+    outs = [torch.empty_like(s["q_blk"]) for s in sets]
+    Ls = [torch.empty(b, dtype=torch.int32, device=dev) for _ in sets]
+    Cs = [torch.empty(b, dtype=torch.int32, device=dev) for _ in sets]
+    ws = binding.attention_workspace(dev, binding.simsd_verify_attention_workspace(
+        b, B, Hq, Hkv, d, max_prefix))
+    stream = torch.cuda.current_stream()
+    lib = binding.load_library()
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    # C-ABI arguments marshalled once per input set, so the loop spends no
+    # Python time on checks (the binding's checked wrappers build the same calls)
+    calls = []
+    for j, s in enumerate(sets):
+        rope = (P(s["q_blk"]), P(s["k_blk"]), P(s["start_pos"]), b, B, Hq, Hkv, d,
+                ctypes.c_float(w.rope_base), 0, hs)
+        attn = (P(s["q_blk"]), P(s["k_blk"]), P(s["v_blk"]), P(s["k_pre"]), P(s["v_pre"]),
+                P(s["prefix_offsets"]), P(s["tau"]), P(outs[j]), None, b, B, Hq, Hkv, d,
+                max_prefix, ctypes.c_float(0.0), 0, None, P(ws), ws.numel(), hs)
+        acc = (P(s["p"]), P(s["q"]), P(s["draft"]), P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]),
+               P(Cs[j]), None, None, 0, hs)
+        calls.append((rope, attn, acc))
+
+    def step(i, ev=None):
+        rope, attn, acc = calls[i % len(calls)]
+        rc = lib.simsd_rope_copy(*rope)
+        if ev is not None:
+            ev[0].record(stream)
+        rc |= lib.simsd_verify_attention(*attn)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= lib.simsd_accept(*acc)
+        if rc:
+            raise RuntimeError(f"libsimsd returned {rc}")
+
+    # parity of one step (set 0, fresh inputs) against the oracle, and the CPU baseline
+    step(0)
+    torch.cuda.synchronize()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu_bps, reps, secs, (ref_out, ref_acc) = cpu_baseline(x, threads)
+        err = float(np.abs(outs[0].to(torch.float64).cpu().numpy() - ref_out).max())
+        L_ok = bool(np.array_equal(Ls[0].cpu().numpy(), ref_acc["accept_len"]))
+        tok_ok = bool(((Cs[0].cpu().numpy() == ref_acc["correction"]) | ref_acc["boundary"].astype(bool)).all())
+        log(f"parity: attention max-abs {err:.3e}, accept lengths equal {L_ok}, tokens ok {tok_ok}")
+        if not (err <= 2e-2 and L_ok and tok_ok):
+            print("parity check failed; not timing", file=sys.stderr)
+            sys.exit(1)
+        cpu = {"value": round(cpu_bps, 3), "unit": "blocks/s", "cores": threads, "kind": "oracle",
+               "sample": f"{reps} full batches of the {WORKLOAD} workload ({reps * b} blocks: "
+                         f"RoPE-copy + verify attention + acceptance, fp64 C oracle) in {secs:.1f} s"}
+
+    for i in range(args.warmup):
+        step(i + 1)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i + 1 + args.warmup, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = [a.elapsed_time(z) for a, z in evs]
+    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    ms_per_step = total_ms / args.steps
+    blocks_per_s = b * args.steps / (total_ms / 1e3)
+
+    nbytes, flops = attn_bytes_flops(w, lens)
+    achieved = nbytes / attn_avg_s / 1e9
+    tflops = flops / attn_avg_s / 1e12
+    traffic = counter_traffic()
+    ai = flops / nbytes
+    result = {
+        "metric": METRIC,
+        "value": round(blocks_per_s, 1),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: {w.describe()}", "global_batch": b,
+                   "prefix": max_prefix, "block_B": B, "input_sets_rotated": args.sets,
+                   "step": "rope_copy + verify_attention + accept"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "verify_attn_kernel",
+                     "avg_launch_us": round(attn_avg_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "attention_mfma": {"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                           "ceiling_at_hbm_peak": round(min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS), 4),
+                           "flops_per_launch": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

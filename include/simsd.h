@@ -1,0 +1,203 @@
+/*
+ * simsd.h -- C ABI of libsimsd, the MI355X (gfx950) verification hot path of
+ * SimSD (simple speculative decoding for diffusion language models).
+ *
+ * Sources, cited by page title and section (second-hand summaries of the
+ * SimSD paper, arXiv 2606.02544):
+ *   [nl] "Technische Samenvatting: SimSD - Simple Speculative Decoding in
+ *        Diffusion Language Models" (gist.science/nl/paper/2606.02544)
+ *   [fr] "SimSD: Simple Speculative Decoding in Diffusion Language Models",
+ *        part "Resume Technique" (gist.science/fr/paper/2606.02544)
+ *
+ * The verification step of one speculative round (see [nl]/[fr] Methodologie
+ * 4): the target model reads the cached prompt, a data section D of B draft
+ * tokens and a mask section D~ of B [MASK] slots (Methodologie 1), rotates the
+ * block's queries and keys with the RoPE copy rule (Methodologie 3), runs one
+ * attention pass under the temporal mask (Methodologie 2), and finally the
+ * drafts are accepted or rejected along the draft's temporal order. The three
+ * entry points below are the attention-layer and acceptance parts of that
+ * step; projections, MLP and LM head are outside this library.
+ *
+ * Conventions common to every entry point
+ *   - Every tensor argument is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or synchronises; each call enqueues its
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     returns at once.
+ *   - The return value is a host-detected error code (simsd_status_t). On any
+ *     nonzero return nothing has been launched and no memory was touched.
+ *   - Data-dependent problems are reported per sequence in the optional device
+ *     array `status` (int32 [b]): each call ORs its SIMSD_DEV_* bits into it
+ *     and never clears it, so one zeroed array can collect a whole chain.
+ *   - bf16 is the IEEE-754 binary32 upper half (bfloat16), stored as uint16.
+ *   - Block rows of a sequence are numbered r = 0..2B-1: r < B is the data
+ *     token D_{r+1}, r >= B the mask slot D~_{r-B+1}.
+ *   - tau[s][k-1] is the temporal step label tau(k) in 1..B of response
+ *     position k (the step map of Methodologie 2; the pages call the map mu and
+ *     its values tau). D_k and D~_k share tau(k).
+ *   - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef SIMSD_H
+#define SIMSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SIMSD_OK = 0,
+  SIMSD_ERR_NULL = 1,      /* a required pointer is NULL */
+  SIMSD_ERR_SIZE = 2,      /* b < 1, B outside 1..64, Hq/Hkv < 1, V < 1, max_prefix < 0, ... */
+  SIMSD_ERR_HEADS = 3,     /* Hq is not a multiple of Hkv */
+  SIMSD_ERR_HEAD_DIM = 4,  /* d is not 64 or 128 */
+  SIMSD_ERR_FLAGS = 5,     /* unknown or conflicting flag bits */
+  SIMSD_ERR_WORKSPACE = 6, /* workspace NULL, too small or not 256-byte aligned */
+  SIMSD_ERR_ALIGN = 7,     /* a tensor pointer is not 16-byte aligned */
+  SIMSD_ERR_LAUNCH = 8,    /* the HIP runtime refused a launch (see simsd_last_hip_error) */
+  SIMSD_ERR_SCALE = 9      /* rope_base <= 0 or a non-finite scale */
+} simsd_status_t;
+
+/* Device status bits (int32 per sequence, OR-ed in). */
+#define SIMSD_DEV_BAD_TAU 1       /* tau[s] is not a permutation of 1..B */
+#define SIMSD_DEV_ZERO_RESIDUAL 2 /* acceptance: residual mass 0, correction drawn from p */
+#define SIMSD_DEV_Q_ZERO 4        /* acceptance: q(x) == 0 met (accepted iff p(x) > 0) */
+#define SIMSD_DEV_BAD_TOKEN 8     /* acceptance: a draft id outside [0, V) (step rejected) */
+#define SIMSD_DEV_BAD_PREFIX 16   /* attention: P_s < 0 or P_s > max_prefix (P_s clamped into range) */
+
+/* simsd_rope_copy flags */
+#define SIMSD_ROPE_HALF 0u        /* rotate-half pairing (i, i + d/2) (default) */
+#define SIMSD_ROPE_INTERLEAVED 1u /* pairing (2i, 2i+1) */
+#define SIMSD_ROPE_NO_COPY 2u     /* ablation: D~_k at start + B + k - 1 instead of start + k - 1 */
+
+/* simsd_verify_attention flags: data-row rule (2 bits) | output dtype */
+#define SIMSD_DATA_CAUSAL 0u /* D_i sees the prefix and D_j with tau(j) <= tau(i) (default) */
+#define SIMSD_DATA_BIDIR 1u  /* D_i sees the prefix and every D_j */
+#define SIMSD_DATA_SKIP 2u   /* data rows are not computed; their out/lse rows are untouched */
+#define SIMSD_OUT_F32 4u     /* out is fp32 instead of bf16 */
+
+/*
+ * simsd_rope_copy -- rotary position embedding of the block's queries and
+ * keys with the copy rule ([nl]/[fr] Methodologie 3: each mask slot D~_k reuses
+ * the RoPE index of its paired data token D_k).
+ *
+ *   q_blk      bf16 [b][2B][Hq][d], rotated in place
+ *   k_blk      bf16 [b][2B][Hkv][d], rotated in place
+ *   start_pos  int32 [b]: position of D_1 of each sequence (normally its
+ *              prefix length P_s). D_k and D~_k both sit at start_pos + k - 1;
+ *              with SIMSD_ROPE_NO_COPY, D~_k sits at start_pos + B + k - 1.
+ *   rope_base  base of the frequencies: frequency i = 0..d/2-1 turns by
+ *              pos * rope_base^(-2i/d) radians. Angles, cos/sin and the
+ *              rotation are evaluated in fp64; each result is rounded to bf16
+ *              once (round to nearest even).
+ *   flags      SIMSD_ROPE_* bits.
+ * The cached prefix keys are not touched (they were rotated when cached).
+ * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, heads<1), _HEAD_DIM,
+ * _FLAGS, _SCALE (rope_base <= 0 or not finite), _ALIGN, _LAUNCH.
+ */
+int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, int B, int Hq,
+                    int Hkv, int d, float rope_base, uint32_t flags, void* stream);
+
+/*
+ * simsd_verify_attention -- one attention pass of the verification forward
+ * over the cached prefix plus the paired block, under the temporal mask
+ * ([nl]/[fr] Methodologie 2 and 4; the prefix comes from the KV cache,
+ * [nl] Belangrijkste Bijdragen 3 / [fr] Principales Contributions).
+ *
+ * Allowed keys of a query in block row r of sequence s:
+ *   - every cached prefix position of the sequence;
+ *   - mask slot D~_i: data tokens D_j with tau(j) < tau(i) and mask slots D~_j
+ *     with tau(j) >= tau(i) (itself included);
+ *   - data token D_i (the pages give no rule; chosen by flags):
+ *     SIMSD_DATA_CAUSAL: D_j with tau(j) <= tau(i); SIMSD_DATA_BIDIR: every
+ *     D_j; never a mask slot. SIMSD_DATA_SKIP: the row is not computed.
+ * out = softmax over the allowed keys only (masked keys enter neither the
+ * maximum nor the sum) of scale * q.k, applied to the values.
+ *
+ *   q_blk, k_blk, v_blk  bf16 [b][2B][Hq|Hkv|Hkv][d] (post-RoPE)
+ *   k_pre, v_pre         bf16 [sum_s P_s][Hkv][d]: packed prefix cache, rows
+ *                        prefix_offsets[s] .. prefix_offsets[s+1]-1 belong to s
+ *   prefix_offsets       int32 [b+1], non-decreasing, offsets[0] = 0
+ *   tau                  int32 [b][B]
+ *   out                  [b][2B][Hq][d], bf16 (or fp32 with SIMSD_OUT_F32)
+ *   lse                  optional fp32 [b][2B][Hq]: natural-log sum of exp of
+ *                        the allowed scores (NULL to skip)
+ *   max_prefix           host int >= every P_s; it sizes the launch. A
+ *                        sequence with P_s > max_prefix (or P_s < 0) is
+ *                        computed with P_s clamped into [0, max_prefix] and
+ *                        flagged SIMSD_DEV_BAD_PREFIX.
+ *   scale                softmax scale; <= 0 selects 1/sqrt(d)
+ *   status               optional int32 [b]; SIMSD_DEV_BAD_TAU (output of
+ *                        that sequence is then unspecified), _BAD_PREFIX
+ *   workspace, ws_bytes  device scratch of at least
+ *                        simsd_verify_attention_workspace(...) bytes, 256-byte
+ *                        aligned. Its first 256 KiB hold one counter word per
+ *                        (sequence, KV head, row slice); the rest holds
+ *                        per-split partial results. The first 256 KiB must be
+ *                        ZERO before the first call that uses the buffer;
+ *                        every call, whatever its sizes, leaves them zero
+ *                        again. Calls that share a workspace must not run
+ *                        concurrently. b * Hkv * ceil(2B * Hq/Hkv / 128) must
+ *                        not exceed 65536 (else SIMSD_ERR_SIZE).
+ * Numerics: bf16 inputs, fp32 MFMA accumulation and fp32 softmax.
+ * Errors: SIMSD_ERR_NULL, _SIZE, _HEADS, _HEAD_DIM, _FLAGS, _WORKSPACE,
+ * _ALIGN, _SCALE, _LAUNCH.
+ */
+int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_blk,
+                           const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                           const int32_t* tau, void* out, float* lse, int b, int B, int Hq,
+                           int Hkv, int d, int max_prefix, float scale, uint32_t flags,
+                           int32_t* status, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes simsd_verify_attention needs for these sizes (0 on bad
+ * sizes). */
+size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix);
+
+/*
+ * simsd_accept -- rejection-sampling acceptance along the draft's temporal
+ * order ([nl]/[fr] Methodologie 4: standard rejection sampling in the order
+ * the draft induced; the longest accepted prefix is committed).
+ *
+ *   p, q          fp32 [b][B][V]: target and draft probabilities at the B
+ *                 response positions, in natural position order
+ *   draft_tokens  int32 [b][B]: draft token id at each position
+ *   tau           int32 [b][B]
+ *   uniforms      fp32 [b][B+1] in [0,1): u_t (t = 1..B) decides temporal
+ *                 step t, u_{B+1} draws the correction
+ *   accept_len    int32 [b] out: L = number of leading accepted steps (0..B)
+ *   correction_token int32 [b] out: -1 when L == B (no bonus slot), else the
+ *                 token drawn for position tau^-1(L+1)
+ * Per sequence: for t = 1..B with k = tau^-1(t) and x = draft[k], step t is
+ * accepted iff u_t < min(1, p[k][x] / q[k][x]) (IEEE fp32 division; if
+ * q[k][x] == 0 the step is accepted iff p[k][x] > 0). On the first rejection
+ * the correction is the smallest y whose running sum of the residual
+ * max(0, p[k][y] - q[k][y]) (fp32 terms, fp64 sums) exceeds u_{B+1} * Z, Z
+ * the total residual. If Z == 0 the same draw is made from p[k]
+ * (SIMSD_DEV_ZERO_RESIDUAL). Decisions are bit-reproducible; the drawn token
+ * can differ from a sequential-sum reference only when u_{B+1} * Z lies within
+ * rounding of a CDF step.
+ *   status        optional int32 [b]: SIMSD_DEV_BAD_TAU (then L = 0,
+ *                 correction -1), _ZERO_RESIDUAL, _Q_ZERO, _BAD_TOKEN
+ *   workspace     unused by this version (pass NULL, 0); reserved.
+ * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, V<1), _ALIGN, _LAUNCH.
+ */
+int simsd_accept(const float* p, const float* q, const int32_t* draft_tokens, const int32_t* tau,
+                 const float* uniforms, int b, int B, int V, int32_t* accept_len,
+                 int32_t* correction_token, int32_t* status, void* workspace, size_t ws_bytes,
+                 void* stream);
+
+/* Workspace bytes simsd_accept needs (0 for this version). */
+size_t simsd_accept_workspace(int b, int B, int V);
+
+/* Static text for a simsd_status_t value. */
+const char* simsd_status_string(int code);
+
+/* The hipError_t of the last failed launch in this thread (0 if none). */
+int simsd_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIMSD_H */

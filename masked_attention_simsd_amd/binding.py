@@ -1,0 +1,212 @@
+"""ctypes binding of libsimsd (the C ABI in include/simsd.h).
+
+Argument marshalling only: each function checks tensor devices, dtypes and
+shapes, passes raw device pointers and the current HIP stream, and raises
+SimsdError on a nonzero return code. All computation happens in the HIP
+kernels of libsimsd.so; there is no fallback path. If the library has not
+been built the first call raises (build it with
+``python -m masked_attention_simsd_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsimsd.so")
+
+# flag and status values, as in include/simsd.h
+SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY = 0, 1, 2
+SIMSD_DATA_CAUSAL, SIMSD_DATA_BIDIR, SIMSD_DATA_SKIP, SIMSD_OUT_F32 = 0, 1, 2, 4
+SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
+SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX = 8, 16
+
+EXPORTS = (
+    "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_workspace",
+    "simsd_accept", "simsd_accept_workspace", "simsd_status_string", "simsd_last_hip_error",
+)
+
+
+class SimsdError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsimsd.so (in-tree). Raises if it is missing: there is no fallback."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m masked_attention_simsd_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I, U, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+        lib.simsd_rope_copy.argtypes = [P, P, P, I, I, I, I, I, F, U, P]
+        lib.simsd_rope_copy.restype = I
+        lib.simsd_verify_attention.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, U, P, P, Z, P]
+        lib.simsd_verify_attention.restype = I
+        lib.simsd_verify_attention_workspace.argtypes = [I, I, I, I, I, I]
+        lib.simsd_verify_attention_workspace.restype = Z
+        lib.simsd_accept.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, Z, P]
+        lib.simsd_accept.restype = I
+        lib.simsd_accept_workspace.argtypes = [I, I, I]
+        lib.simsd_accept_workspace.restype = Z
+        lib.simsd_status_string.argtypes = [I]
+        lib.simsd_status_string.restype = ctypes.c_char_p
+        lib.simsd_last_hip_error.argtypes = []
+        lib.simsd_last_hip_error.restype = I
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        lib = load_library()
+        msg = lib.simsd_status_string(rc).decode()
+        if rc == 8:
+            msg += f" (hipError {lib.simsd_last_hip_error()})"
+        raise SimsdError(fn, rc, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, dims=None, device=True):
+    if not torch.is_tensor(t):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+
+
+def simsd_rope_copy(q_blk, k_blk, start_pos, rope_base: float = 10000.0, flags: int = 0,
+                    stream=None):
+    """In-place RoPE with the copy rule. q_blk [b][2B][Hq][d], k_blk [b][2B][Hkv][d] bf16,
+    start_pos int32 [b]."""
+    _need(q_blk, "q_blk", torch.bfloat16, 4)
+    _need(k_blk, "k_blk", torch.bfloat16, 4)
+    _need(start_pos, "start_pos", torch.int32, 1)
+    b, twoB, Hq, d = q_blk.shape
+    if twoB % 2 or k_blk.shape[0] != b or k_blk.shape[1] != twoB or k_blk.shape[3] != d:
+        raise ValueError("q_blk / k_blk shapes disagree")
+    if start_pos.shape[0] != b:
+        raise ValueError("start_pos must have b entries")
+    rc = load_library().simsd_rope_copy(_ptr(q_blk), _ptr(k_blk), _ptr(start_pos), b, twoB // 2,
+                                        Hq, k_blk.shape[2], d, float(rope_base), flags,
+                                        _stream(stream))
+    _check("simsd_rope_copy", rc)
+
+
+def simsd_verify_attention_workspace(b: int, B: int, Hq: int, Hkv: int, d: int,
+                                     max_prefix: int) -> int:
+    return int(load_library().simsd_verify_attention_workspace(b, B, Hq, Hkv, d, max_prefix))
+
+
+_ws_cache: dict = {}
+
+
+def attention_workspace(device, nbytes: int):
+    """A zero-initialised workspace of at least nbytes on `device`, reused across
+    calls (every call leaves its counters zero). Calls sharing it must not
+    overlap, so use it from one stream."""
+    key = torch.device(device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key)
+        _ws_cache[key] = ws
+    return ws
+
+
+def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out=None,
+                           lse=None, max_prefix: int | None = None, scale: float = 0.0,
+                           flags: int = 0, status=None, workspace=None, stream=None):
+    """Verify attention. Returns out ([b][2B][Hq][d], bf16 or fp32 with SIMSD_OUT_F32).
+
+    max_prefix: host int >= every prefix length; if None it is read back from
+    prefix_offsets (a device-to-host copy, so not for timed loops).
+    """
+    for t, n in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk")):
+        _need(t, n, torch.bfloat16, 4)
+    for t, n in ((k_pre, "k_pre"), (v_pre, "v_pre")):
+        _need(t, n, torch.bfloat16, 3)
+    _need(prefix_offsets, "prefix_offsets", torch.int32, 1)
+    _need(tau, "tau", torch.int32, 2)
+    b, twoB, Hq, d = q_blk.shape
+    B = twoB // 2
+    Hkv = k_blk.shape[2]
+    if (twoB % 2 or tuple(k_blk.shape) != (b, twoB, Hkv, d) or tuple(v_blk.shape) != (b, twoB, Hkv, d)
+            or k_pre.shape[1:] != (Hkv, d) or v_pre.shape != k_pre.shape
+            or prefix_offsets.shape[0] != b + 1 or tuple(tau.shape) != (b, B)):
+        raise ValueError("inconsistent shapes")
+    if max_prefix is None:
+        off = prefix_offsets.cpu()
+        max_prefix = int((off[1:] - off[:-1]).max()) if b > 0 else 0
+    out_f32 = bool(flags & SIMSD_OUT_F32)
+    if out is None:
+        out = torch.empty_like(q_blk, dtype=torch.float32 if out_f32 else torch.bfloat16)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, 4)
+    if tuple(out.shape) != tuple(q_blk.shape):
+        raise ValueError("out shape must equal q_blk shape")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    need = simsd_verify_attention_workspace(b, B, Hq, Hkv, d, max_prefix)
+    if workspace is None:
+        workspace = attention_workspace(q_blk.device, need)
+    rc = load_library().simsd_verify_attention(
+        _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre) if k_pre.numel() else None,
+        _ptr(v_pre) if v_pre.numel() else None, _ptr(prefix_offsets), _ptr(tau), _ptr(out),
+        _ptr(lse), b, B, Hq, Hkv, d, int(max_prefix), float(scale), flags, _ptr(status),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("simsd_verify_attention", rc)
+    return out
+
+
+def simsd_accept(p, q, draft_tokens, tau, uniforms, accept_len=None, correction_token=None,
+                 status=None, stream=None):
+    """Rejection-sampling acceptance. Returns (accept_len, correction_token), int32 [b]."""
+    _need(p, "p", torch.float32, 3)
+    _need(q, "q", torch.float32, 3)
+    _need(draft_tokens, "draft_tokens", torch.int32, 2)
+    _need(tau, "tau", torch.int32, 2)
+    _need(uniforms, "uniforms", torch.float32, 2)
+    b, B, V = p.shape
+    if (tuple(q.shape) != (b, B, V) or tuple(draft_tokens.shape) != (b, B)
+            or tuple(tau.shape) != (b, B) or tuple(uniforms.shape) != (b, B + 1)):
+        raise ValueError("inconsistent shapes")
+    if accept_len is None:
+        accept_len = torch.empty(b, dtype=torch.int32, device=p.device)
+    if correction_token is None:
+        correction_token = torch.empty(b, dtype=torch.int32, device=p.device)
+    _need(accept_len, "accept_len", torch.int32, 1)
+    _need(correction_token, "correction_token", torch.int32, 1)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    rc = load_library().simsd_accept(_ptr(p), _ptr(q), _ptr(draft_tokens), _ptr(tau),
+                                     _ptr(uniforms), b, B, V, _ptr(accept_len),
+                                     _ptr(correction_token), _ptr(status), None, 0,
+                                     _stream(stream))
+    _check("simsd_accept", rc)
+    return accept_len, correction_token

@@ -1,0 +1,158 @@
+// simsd_api.hip -- the C ABI of libsimsd (declared in include/simsd.h).
+//
+// Host-side argument checks happen here, before anything is enqueued; the
+// kernels live in rope_copy.hip, verify_attention.hip and accept.hip. No entry
+// point allocates, frees or synchronises.
+#include "simsd.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "simsd_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return SIMSD_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return SIMSD_ERR_LAUNCH;
+}
+
+int check_common(int b, int B, int Hq, int Hkv, int d) {
+  if (b < 1 || B < 1 || B > 64 || Hq < 1 || Hkv < 1) return SIMSD_ERR_SIZE;
+  if (Hq % Hkv != 0) return SIMSD_ERR_HEADS;
+  if (d != 64 && d != 128) return SIMSD_ERR_HEAD_DIM;
+  return SIMSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, int B, int Hq,
+                    int Hkv, int d, float rope_base, uint32_t flags, void* stream) {
+  if (!q_blk || !k_blk || !start_pos) return SIMSD_ERR_NULL;
+  int rc = check_common(b, B, Hq, Hkv, d);
+  if (rc) return rc;
+  if (flags & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY)) return SIMSD_ERR_FLAGS;
+  if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return SIMSD_ERR_SCALE;
+  if (!aligned16(q_blk) || !aligned16(k_blk)) return SIMSD_ERR_ALIGN;
+  simsd::RopeArgs a{};
+  a.q = static_cast<uint16_t*>(q_blk);
+  a.k = static_cast<uint16_t*>(k_blk);
+  a.start_pos = start_pos;
+  a.b = b, a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.d = d;
+  a.base = static_cast<double>(rope_base);
+  a.interleaved = (flags & SIMSD_ROPE_INTERLEAVED) ? 1 : 0;
+  a.no_copy = (flags & SIMSD_ROPE_NO_COPY) ? 1 : 0;
+  return launch_status(simsd::launch_rope_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix) {
+  if (check_common(b, B, Hq, Hkv, d) || max_prefix < 0) return 0;
+  if (static_cast<long>(b) * Hkv * ((2L * B * (Hq / Hkv) + 127) / 128) > simsd::kAttnMaxUnits) return 0;
+  // The data-row rule changes the row count and so the plan: size for both.
+  const size_t all_rows = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 0).total_bytes;
+  const size_t slots_only = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 2).total_bytes;
+  return all_rows > slots_only ? all_rows : slots_only;
+}
+
+int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_blk,
+                           const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                           const int32_t* tau, void* out, float* lse, int b, int B, int Hq,
+                           int Hkv, int d, int max_prefix, float scale, uint32_t flags,
+                           int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+  if (!q_blk || !k_blk || !v_blk || !prefix_offsets || !tau || !out) return SIMSD_ERR_NULL;
+  if (max_prefix > 0 && (!k_pre || !v_pre)) return SIMSD_ERR_NULL;
+  int rc = check_common(b, B, Hq, Hkv, d);
+  if (rc) return rc;
+  if (max_prefix < 0) return SIMSD_ERR_SIZE;
+  const uint32_t rule = flags & 3u;
+  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32))) return SIMSD_ERR_FLAGS;
+  if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
+      (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)))
+    return SIMSD_ERR_ALIGN;
+  const simsd::AttnPlan plan = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, static_cast<int>(rule));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || ws_bytes < plan.total_bytes)
+    return SIMSD_ERR_WORKSPACE;
+
+  simsd::AttnArgs a{};
+  a.q_blk = static_cast<const uint16_t*>(q_blk);
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.k_pre = static_cast<const uint16_t*>(k_pre);
+  a.v_pre = static_cast<const uint16_t*>(v_pre);
+  a.offsets = prefix_offsets;
+  a.tau = tau;
+  a.out = out;
+  a.lse = lse;
+  a.status = status;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + plan.counters_bytes);
+  a.part_o = reinterpret_cast<float*>(ws + plan.counters_bytes + plan.ml_bytes);
+  a.b = b, a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv, a.d = d;
+  a.row0 = rule == SIMSD_DATA_SKIP ? B : 0;
+  a.nrows = rule == SIMSD_DATA_SKIP ? B : 2 * B;
+  a.M = a.nrows * a.G;
+  a.row_slices = plan.row_slices;
+  a.chunk = plan.chunk;
+  a.nsplit = plan.nsplit;
+  a.max_prefix = max_prefix;
+  if (static_cast<long>(b) * Hkv * plan.row_slices > simsd::kAttnMaxUnits) return SIMSD_ERR_SIZE;
+  const long total = static_cast<long>(b) * Hkv * plan.row_slices * plan.nsplit;
+  if (total > (1L << 30)) return SIMSD_ERR_SIZE;
+  a.total_real = static_cast<int>(total);
+  a.total_grid = static_cast<int>((total + 7) / 8 * 8);
+  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt(static_cast<float>(d));
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.data_rule = static_cast<int>(rule);
+  a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
+  return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
+}
+
+size_t simsd_accept_workspace(int b, int B, int V) {
+  (void)b, (void)B, (void)V;
+  return 0;
+}
+
+int simsd_accept(const float* p, const float* q, const int32_t* draft_tokens, const int32_t* tau,
+                 const float* uniforms, int b, int B, int V, int32_t* accept_len,
+                 int32_t* correction_token, int32_t* status, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  (void)workspace, (void)ws_bytes;
+  if (!p || !q || !draft_tokens || !tau || !uniforms || !accept_len || !correction_token)
+    return SIMSD_ERR_NULL;
+  if (b < 1 || B < 1 || B > 64 || V < 1) return SIMSD_ERR_SIZE;
+  if (!aligned16(p) || !aligned16(q)) return SIMSD_ERR_ALIGN;
+  simsd::AcceptArgs a{};
+  a.p = p, a.q = q, a.draft = draft_tokens, a.tau = tau, a.u = uniforms;
+  a.b = b, a.B = B, a.V = V;
+  a.accept_len = accept_len, a.correction = correction_token, a.status = status;
+  return launch_status(simsd::launch_accept(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* simsd_status_string(int code) {
+  switch (code) {
+    case SIMSD_OK: return "ok";
+    case SIMSD_ERR_NULL: return "a required pointer is NULL";
+    case SIMSD_ERR_SIZE: return "a size argument is out of range";
+    case SIMSD_ERR_HEADS: return "Hq is not a multiple of Hkv";
+    case SIMSD_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case SIMSD_ERR_FLAGS: return "unknown or conflicting flags";
+    case SIMSD_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
+    case SIMSD_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case SIMSD_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case SIMSD_ERR_SCALE: return "rope_base or scale out of range";
+    default: return "unknown status";
+  }
+}
+
+int simsd_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

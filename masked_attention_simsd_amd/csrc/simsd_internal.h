@@ -1,0 +1,117 @@
+// simsd_internal.h -- device helpers and launcher declarations shared by the
+// gfx950 kernels of libsimsd. Internal to the library (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace simsd {
+
+constexpr int kWave = 64;
+
+// Extra device status bit (kept beside the public ones in simsd.h).
+constexpr int kDevBadTau = 1;
+constexpr int kDevZeroResidual = 2;
+constexpr int kDevQZero = 4;
+constexpr int kDevBadToken = 8;
+constexpr int kDevBadPrefix = 16;
+
+// bf16 <-> fp32. bf16 is the upper half of an IEEE binary32.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// fp64 -> bf16 with a single rounding (nearest even). The double is first
+// narrowed to fp32 with round-to-odd, which keeps enough information for the
+// second, nearest-even narrowing to equal a direct one (fp32 carries 16 more
+// significand bits than bf16).
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  float f = static_cast<float>(x);  // nearest even
+  double back = static_cast<double>(f);
+  if (back != x && !__builtin_isnan(x) && !__builtin_isinf(f)) {
+    uint32_t u = __float_as_uint(f);
+    // step toward zero if the nearest-even result overshot in magnitude
+    if (__builtin_fabs(back) > __builtin_fabs(x)) u -= 1u;
+    u |= 1u;  // round to odd: inexact results get an odd last bit
+    f = __uint_as_float(u);
+  }
+  return f32_to_bf16(f);
+}
+
+struct RopeArgs {
+  uint16_t* q;
+  uint16_t* k;
+  const int32_t* start_pos;
+  int b, B, Hq, Hkv, d;
+  double base;
+  int interleaved, no_copy;
+};
+
+struct AttnArgs {
+  const uint16_t* q_blk;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  const uint16_t* k_pre;
+  const uint16_t* v_pre;
+  const int32_t* offsets;
+  const int32_t* tau;
+  void* out;
+  float* lse;
+  int32_t* status;
+  float* part_o;      // [unit_slice][split][wave][qb][dblk][lane] x 4 floats
+  float* part_ml;     // [unit_slice][split][row] x (m, l)
+  int32_t* counters;  // [unit_slice]
+  int b, B, Hq, Hkv, G, d;
+  int row0, nrows;    // block rows computed: [row0, row0 + nrows)
+  int M;              // query rows per (sequence, KV head) = nrows * G
+  int row_slices;     // ceil(M / rows per workgroup)
+  int chunk;          // prefix keys per split (multiple of the key tile)
+  int nsplit;         // splits per (sequence, KV head, row slice)
+  int max_prefix;
+  int total_real;     // b * Hkv * row_slices * nsplit
+  int total_grid;     // total_real rounded up to a multiple of 8
+  float scale_log2;   // softmax scale * log2(e)
+  int data_rule;      // 0 causal, 1 bidirectional, 2 skip data rows
+  int out_f32;
+};
+
+struct AttnPlan {
+  int nwc, qb;        // compute waves and 16-row query blocks per wave
+  int rows_per_wg;
+  int row_slices;
+  int chunk, nsplit;
+  size_t counters_bytes, ml_bytes, o_bytes, total_bytes;
+};
+
+struct AcceptArgs {
+  const float* p;
+  const float* q;
+  const int32_t* draft;
+  const int32_t* tau;
+  const float* u;
+  int b, B, V;
+  int32_t* accept_len;
+  int32_t* correction;
+  int32_t* status;
+};
+
+constexpr int kAttnTileKeys = 64;  // keys staged per tile
+constexpr int kAttnThreads = 256;
+constexpr int kAttnMaxUnits = 65536;  // (sequence, KV head, row slice) units per call
+
+AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule);
+
+hipError_t launch_rope_copy(const RopeArgs& a, hipStream_t stream);
+hipError_t launch_verify_attention(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+}  // namespace simsd

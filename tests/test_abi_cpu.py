@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/simsd.h, and rejects bad arguments on the host before any
+launch (every call below returns before touching the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from masked_attention_simsd_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "simsd.h")
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced on these paths
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(simsd_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libsimsd.so not built")
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(10):
+        assert lib.simsd_status_string(code)
+    assert lib.simsd_status_string(0) == b"ok"
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, off=FAKE, tau=FAKE, out=FAKE, lse=None,
+             b=2, B=4, Hq=8, Hkv=2, d=128, maxp=100, scale=0.0, flags=0, status=None,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.simsd_verify_attention(a["q"], a["k"], a["v"], a["kp"], a["vp"], a["off"], a["tau"],
+                                      a["out"], a["lse"], a["b"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                      a["maxp"], a["scale"], a["flags"], a["status"], a["ws"],
+                                      a["wsb"], None)
+
+
+def test_attention_host_errors(lib):
+    assert _attn(lib, q=None) == 1
+    assert _attn(lib, kp=None) == 1
+    assert _attn(lib, kp=None, vp=None, maxp=0, ws=None) == 6  # empty prefix needs no cache
+    assert _attn(lib, b=0) == 2
+    assert _attn(lib, B=65) == 2
+    assert _attn(lib, B=0) == 2
+    assert _attn(lib, maxp=-1) == 2
+    assert _attn(lib, Hq=6, Hkv=4) == 3
+    assert _attn(lib, d=96) == 4
+    assert _attn(lib, flags=3) == 5
+    assert _attn(lib, flags=8) == 5
+    assert _attn(lib, scale=float("nan")) == 9
+    assert _attn(lib, out=MISALIGNED) == 7
+    assert _attn(lib, ws=None) == 6
+    assert _attn(lib, ws=MISALIGNED) == 6
+    need = lib.simsd_verify_attention_workspace(2, 4, 8, 2, 128, 100)
+    assert need > 0
+    assert _attn(lib, wsb=need - 1) == 6
+
+
+def test_workspace_sizes(lib):
+    assert lib.simsd_verify_attention_workspace(0, 4, 8, 2, 128, 100) == 0
+    assert lib.simsd_verify_attention_workspace(1, 4, 8, 3, 128, 100) == 0
+    assert lib.simsd_verify_attention_workspace(1, 4, 8, 2, 100, 100) == 0
+    assert lib.simsd_verify_attention_workspace(1, 4, 8, 2, 128, -1) == 0
+    for cfg in [(16, 8, 32, 8, 128, 4096), (8, 16, 32, 8, 128, 16384), (64, 8, 32, 8, 128, 8192),
+                (1, 4, 1, 1, 64, 32), (1, 64, 32, 8, 128, 100)]:
+        n = lib.simsd_verify_attention_workspace(*cfg)
+        assert n % 256 == 0 and 0 < n < (1 << 31)
+    assert lib.simsd_accept_workspace(16, 8, 32768) == 0
+
+
+def test_rope_host_errors(lib):
+    f = lambda **kw: lib.simsd_rope_copy(kw.get("q", FAKE), kw.get("k", FAKE), kw.get("sp", FAKE),
+                                         kw.get("b", 1), kw.get("B", 4), kw.get("Hq", 8),
+                                         kw.get("Hkv", 2), kw.get("d", 64),
+                                         kw.get("base", 10000.0), kw.get("flags", 0), None)
+    assert f(q=None) == 1
+    assert f(sp=None) == 1
+    assert f(B=65) == 2
+    assert f(Hq=7) == 3
+    assert f(d=32) == 4
+    assert f(flags=4) == 5
+    assert f(base=0.0) == 9
+    assert f(base=float("inf")) == 9
+    assert f(k=MISALIGNED) == 7
+
+
+def test_accept_host_errors(lib):
+    f = lambda **kw: lib.simsd_accept(kw.get("p", FAKE), kw.get("q", FAKE), FAKE, FAKE, FAKE,
+                                      kw.get("b", 1), kw.get("B", 4), kw.get("V", 16),
+                                      kw.get("L", FAKE), FAKE, None, None, 0, None)
+    assert f(p=None) == 1
+    assert f(L=None) == 1
+    assert f(b=0) == 2
+    assert f(B=65) == 2
+    assert f(V=0) == 2
+    assert f(q=MISALIGNED) == 7
