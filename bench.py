@@ -106,6 +106,45 @@ def cpu_baseline(x, threads):
     return w.b * reps / el, reps, el, first
 
 
+def copy_calibration(mib: int):
+    """A plain device copy of known size (repeated 10 times), used to scale the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 10}), flush=True)
+
+
+def summarize_rocprof(path: str):
+    """Reduce rocprofv3 CSV output under `path` to per-kernel lines: average
+    duration from *kernel_stats.csv, mean counter value per dispatch from
+    *counter_collection.csv."""
+    import csv
+    import glob
+    import statistics
+
+    for f in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# kernel stats: {os.path.relpath(f, path)}")
+        for r in csv.DictReader(open(f)):
+            print(f"{r['Name'][:90]:90s} calls {int(r['Calls']):6d}  avg_us {float(r['AverageNs']) / 1e3:10.3f}"
+                  f"  min_us {float(r['MinNs']) / 1e3:10.3f}  max_us {float(r['MaxNs']) / 1e3:10.3f}"
+                  f"  pct {float(r['Percentage']):6.2f}")
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        print(f"# counters: {os.path.relpath(f, path)}")
+        acc = {}
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"][:90], r["Counter_Name"])
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+        for (k, c), v in sorted(acc.items()):
+            print(f"{k:90s} {c:12s} dispatches {len(v):5d}  mean_per_dispatch {statistics.fmean(v):16.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,7 +152,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR", help="summarise rocprofv3 CSV output")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -143,6 +191,7 @@ def main():
     Cs = [torch.empty(b, dtype=torch.int32, device=dev) for _ in sets]
     ws = binding.attention_workspace(dev, binding.simsd_verify_attention_workspace(
         b, B, Hq, Hkv, d, max_prefix))
+    ws_acc = binding.accept_workspace(dev, binding.simsd_accept_workspace(b, B, w.V))
     stream = torch.cuda.current_stream()
     lib = binding.load_library()
     P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
@@ -157,17 +206,13 @@ def main():
                 P(s["prefix_offsets"]), P(s["tau"]), P(outs[j]), None, b, B, Hq, Hkv, d,
                 max_prefix, ctypes.c_float(0.0), 0, None, P(ws), ws.numel(), hs)
         acc = (P(s["p"]), P(s["q"]), P(s["draft"]), P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]),
-               P(Cs[j]), None, None, 0, hs)
+               P(Cs[j]), None, P(ws_acc), ws_acc.numel(), hs)
         calls.append((rope, attn, acc))
 
-    def step(i, ev=None):
+    def step(i):
         rope, attn, acc = calls[i % len(calls)]
         rc = lib.simsd_rope_copy(*rope)
-        if ev is not None:
-            ev[0].record(stream)
         rc |= lib.simsd_verify_attention(*attn)
-        if ev is not None:
-            ev[1].record(stream)
         rc |= lib.simsd_accept(*acc)
         if rc:
             raise RuntimeError(f"libsimsd returned {rc}")
@@ -193,21 +238,27 @@ def main():
     for i in range(args.warmup):
         step(i + 1)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # timed region 1: whole steps (RoPE-copy + verify attention + acceptance)
+    t0, t1 = ev(), ev()
+    t0.record(stream)
     for i in range(args.steps):
-        step(i + 1 + args.warmup, evs[i])
-    t_end.record(stream)
+        step(i + 1 + args.warmup)
+    t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    attn_ms = [a.elapsed_time(z) for a, z in evs]
-    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
     blocks_per_s = b * args.steps / (total_ms / 1e3)
+    # timed region 2: the attention kernel alone, back to back on the same
+    # stream over the rotated input sets (its average launch duration)
+    a0, a1 = ev(), ev()
+    a0.record(stream)
+    for i in range(args.steps):
+        if lib.simsd_verify_attention(*calls[i % len(calls)][1]):
+            raise RuntimeError("simsd_verify_attention failed")
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attn_avg_s = a0.elapsed_time(a1) / args.steps / 1e3
 
     nbytes, flops = attn_bytes_flops(w, lens)
     achieved = nbytes / attn_avg_s / 1e9

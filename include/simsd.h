@@ -179,15 +179,21 @@ size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, in
  * rounding of a CDF step.
  *   status        optional int32 [b]: SIMSD_DEV_BAD_TAU (then L = 0,
  *                 correction -1), _ZERO_RESIDUAL, _Q_ZERO, _BAD_TOKEN
- *   workspace     unused by this version (pass NULL, 0); reserved.
- * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, V<1), _ALIGN, _LAUNCH.
+ *   workspace, ws_bytes  device scratch of at least simsd_accept_workspace()
+ *                 bytes, 256-byte aligned: the first 256 KiB hold one counter
+ *                 word per sequence and must be ZERO before the first call that
+ *                 uses the buffer (every call leaves them zero again); the rest
+ *                 holds per-segment residual masses. Calls sharing a workspace
+ *                 must not run concurrently.
+ * Errors: SIMSD_ERR_NULL, _SIZE (b<1 or b>65536, B not in 1..64, V<1 or
+ * V>2^21), _ALIGN, _WORKSPACE, _LAUNCH.
  */
 int simsd_accept(const float* p, const float* q, const int32_t* draft_tokens, const int32_t* tau,
                  const float* uniforms, int b, int B, int V, int32_t* accept_len,
                  int32_t* correction_token, int32_t* status, void* workspace, size_t ws_bytes,
                  void* stream);
 
-/* Workspace bytes simsd_accept needs (0 for this version). */
+/* Workspace bytes simsd_accept needs for these sizes (0 on bad sizes). */
 size_t simsd_accept_workspace(int b, int B, int V);
 
 /* Static text for a simsd_status_t value. */

@@ -126,16 +126,29 @@ def simsd_verify_attention_workspace(b: int, B: int, Hq: int, Hkv: int, d: int,
 _ws_cache: dict = {}
 
 
-def attention_workspace(device, nbytes: int):
-    """A zero-initialised workspace of at least nbytes on `device`, reused across
-    calls (every call leaves its counters zero). Calls sharing it must not
-    overlap, so use it from one stream."""
-    key = torch.device(device)
+def _cached_workspace(kind: str, device, nbytes: int):
+    key = (kind, torch.device(device))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key[1])
         _ws_cache[key] = ws
     return ws
+
+
+def attention_workspace(device, nbytes: int):
+    """A zero-initialised workspace of at least nbytes on `device` for
+    simsd_verify_attention, reused across calls (every call leaves its counter
+    words zero). Calls sharing it must not overlap, so use it from one stream."""
+    return _cached_workspace("attention", device, nbytes)
+
+
+def accept_workspace(device, nbytes: int):
+    """As attention_workspace, for simsd_accept."""
+    return _cached_workspace("accept", device, nbytes)
+
+
+def simsd_accept_workspace(b: int, B: int, V: int) -> int:
+    return int(load_library().simsd_accept_workspace(b, B, V))
 
 
 def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out=None,
@@ -185,7 +198,7 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
 
 
 def simsd_accept(p, q, draft_tokens, tau, uniforms, accept_len=None, correction_token=None,
-                 status=None, stream=None):
+                 status=None, workspace=None, stream=None):
     """Rejection-sampling acceptance. Returns (accept_len, correction_token), int32 [b]."""
     _need(p, "p", torch.float32, 3)
     _need(q, "q", torch.float32, 3)
@@ -204,9 +217,13 @@ def simsd_accept(p, q, draft_tokens, tau, uniforms, accept_len=None, correction_
     _need(correction_token, "correction_token", torch.int32, 1)
     if status is not None:
         _need(status, "status", torch.int32, 1)
+    need = simsd_accept_workspace(b, B, V)
+    if workspace is None:
+        workspace = accept_workspace(p.device, need)
     rc = load_library().simsd_accept(_ptr(p), _ptr(q), _ptr(draft_tokens), _ptr(tau),
                                      _ptr(uniforms), b, B, V, _ptr(accept_len),
-                                     _ptr(correction_token), _ptr(status), None, 0,
+                                     _ptr(correction_token), _ptr(status), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
                                      _stream(stream))
     _check("simsd_accept", rc)
     return accept_len, correction_token

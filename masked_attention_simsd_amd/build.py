@@ -26,6 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     "-fno-fast-math", "-ffp-contract=fast",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",  # MFMA accumulators in VGPRs: no AGPR copies around VALU work
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

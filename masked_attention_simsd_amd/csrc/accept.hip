@@ -6,102 +6,129 @@
 // standard rejection sampling is applied in the temporal order the draft
 // induced, and the longest accepted prefix is committed.
 //
-// One workgroup (16 waves) per sequence.
-//   Phase 1 (wave 0, one lane per temporal step t): invert tau, gather
-//   p[k][x] and q[k][x] at k = tau^-1(t), take the fp32 ratio, compare with
-//   u_t, and find the first rejected step with one ballot.
-//   Phase 2 (all waves, only if a step was rejected): stream the vocabulary
-//   row of p and q at k* = tau^-1(L+1) once to get each wave's residual mass
-//   max(0, p - q) over a contiguous vocabulary segment (fp64 sums), pick the
-//   segment holding u_{B+1} * Z, and let its wave rescan that segment with a
-//   wave-wide prefix sum to find the first token whose running mass exceeds
-//   the threshold.
-// The vocabulary stream is the only sizeable traffic (2 V fp32 per rejecting
-// sequence), so the kernel is HBM/latency bound; the second read of the
-// chosen segment is served from L2.
+// The step is latency bound, and one CU cannot keep enough misses in flight to
+// stream a 32K-151K vocabulary row quickly, so each sequence is spread over
+// ceil(V / 4096) workgroups of 256 threads (grid: segments x sequences).
+//   Phase 1 (wave 0 of every workgroup, one lane per temporal step t): tau and
+//   the draft ids are read together, tau is inverted in LDS, p[k][x] and
+//   q[k][x] are gathered at k = tau^-1(t), the IEEE fp32 ratio is compared
+//   with u_t, and one ballot gives the first rejected step L. Every workgroup
+//   of a sequence repeats this (a few gathers) so none waits for another.
+//   Phase 2 (only if L < B): each workgroup reads its 4096-entry segment of
+//   the rows p[k*], q[k*] (k* = tau^-1(L+1)), 16 contiguous entries per
+//   thread, and publishes the segment's fp64 residual mass max(0, p - q) with
+//   device-coherent stores. The last workgroup of the sequence (agent-scope
+//   counter) fetches all segment masses at once, forms Z in segment order,
+//   finds the segment holding T = u_{B+1} * Z and rescans it with a
+//   workgroup-wide prefix sum for the first token whose running mass exceeds T.
+// Traffic: 2 V fp32 per rejecting sequence plus one segment re-read.
 #include "simsd_internal.h"
 
 namespace simsd {
 
 namespace {
 
-constexpr int kAccThreads = 1024;
+constexpr int kAccThreads = 256;
 constexpr int kAccWaves = kAccThreads / kWave;
-constexpr int kIter = kWave * 4;  // vocabulary entries per wave iteration
+constexpr int kPerThread = 16;                  // contiguous entries per thread
+constexpr int kSeg = kAccThreads * kPerThread;  // entries per segment / workgroup
 
-__device__ __forceinline__ float4 load4(const float* row, int y, int V, bool vec) {
-  if (vec && y + 3 < V) return *reinterpret_cast<const float4*>(row + y);
-  float4 r;
-  r.x = y < V ? row[y] : 0.0f;
-  r.y = y + 1 < V ? row[y + 1] : 0.0f;
-  r.z = y + 2 < V ? row[y + 2] : 0.0f;
-  r.w = y + 3 < V ? row[y + 3] : 0.0f;
-  return r;
+// Masses of entries y0 .. y0+15 of one row: the residual max(0, p - q) in
+// fp32, or p itself for the zero-residual fallback; entries at or past V are 0.
+__device__ __forceinline__ void load_masses(const float* prow, const float* qrow, int y0, int V,
+                                            bool vec, bool use_p, float w[kPerThread]) {
+  float pv[kPerThread], qv[kPerThread];
+  if (vec && y0 + kPerThread <= V) {
+#pragma unroll
+    for (int j = 0; j < kPerThread / 4; ++j) {
+      const float4 a = *reinterpret_cast<const float4*>(prow + y0 + 4 * j);
+      pv[4 * j] = a.x, pv[4 * j + 1] = a.y, pv[4 * j + 2] = a.z, pv[4 * j + 3] = a.w;
+      const float4 b = use_p ? a : *reinterpret_cast<const float4*>(qrow + y0 + 4 * j);
+      qv[4 * j] = b.x, qv[4 * j + 1] = b.y, qv[4 * j + 2] = b.z, qv[4 * j + 3] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const bool in = y0 + e < V;
+      pv[e] = in ? prow[y0 + e] : 0.0f;
+      qv[e] = (in && !use_p) ? qrow[y0 + e] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const float r = use_p ? pv[e] : pv[e] - qv[e];
+    w[e] = r > 0.0f ? r : 0.0f;
+  }
 }
 
-// Mass of the four entries y .. y+3: the residual max(0, p - q) (fp32), or p
-// itself when the residual is empty.
-__device__ __forceinline__ void masses(const float* prow, const float* qrow, int y, int V,
-                                       bool vec, bool use_p, float w[4]) {
-  float4 pv = load4(prow, y, V, vec);
-  float pa[4] = {pv.x, pv.y, pv.z, pv.w};
-  if (use_p) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = pa[j] > 0.0f ? pa[j] : 0.0f;
-    return;
-  }
-  float4 qv = load4(qrow, y, V, vec);
-  float qa[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float r = pa[j] - qa[j];
-    w[j] = r > 0.0f ? r : 0.0f;
-  }
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave (fp64).
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+// Exclusive prefix sum (thread order) of one fp64 value per thread and the
+// workgroup total, which is computed as last exclusive prefix + last value so
+// that a rescan's running sums end exactly at the segment mass.
+__device__ double block_excl_scan(double v, double* total) {
+  __shared__ double sh_wave[kAccWaves];
+  __shared__ double sh_total;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  double incl = v;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    double o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
+    const double o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
   }
-  return v;
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  if (lane == kWave - 1) sh_wave[wave] = incl;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += sh_wave[w];
+  excl += base;
+  if (tid == kAccThreads - 1) sh_total = excl + v;
+  __syncthreads();
+  *total = sh_total;
+  __syncthreads();  // the shared slots may be reused after this
+  return excl;
+}
+
+__device__ __forceinline__ double thread_sum(const float w[kPerThread]) {
+  double ls = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) ls += static_cast<double>(w[e]);
+  return ls;
 }
 
 __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   __shared__ int inv_s[64];
-  __shared__ int sh_L, sh_stat, sh_done, sh_wstar, sh_pick;
-  __shared__ double seg_sum[kAccWaves];
+  __shared__ int sh_L, sh_stat, sh_last, sh_pick, sh_seg;
+  __shared__ double sh_mass[kMaxAcceptVocab / kSeg];
   __shared__ double sh_T, sh_base;
 
-  const int s = blockIdx.x;
+  const int seg = blockIdx.x, nseg = gridDim.x;
+  const int s = blockIdx.y;
   const int B = a.B, V = a.V;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float u_corr = a.u[static_cast<size_t>(s) * (B + 1) + B];  // requested early
 
   if (wave == 0) {
-    // Invert tau: lane t looks for the unique k with tau(k) = t + 1.
-    int cnt = 0, kk = -1;
-    if (lane < B) {
-      for (int k = 0; k < B; ++k) {
-        if (a.tau[static_cast<size_t>(s) * B + k] == lane + 1) {
-          ++cnt;
-          kk = k;
-        }
-      }
-    }
-    const bool bad = __ballot(lane < B && cnt != 1) != 0ull;
-    if (lane < B) inv_s[lane] = kk;
+    const int t_k = lane < B ? a.tau[static_cast<size_t>(s) * B + lane] : 0;  // tau(lane+1)
+    const int x_k = lane < B ? a.draft[static_cast<size_t>(s) * B + lane] : 0;
+    if (lane < B) inv_s[lane] = -1;
+    // invert: position k = lane writes itself at slot tau(k) - 1; a duplicate or
+    // out-of-range label makes tau invalid
+    const bool in_range = lane < B && t_k >= 1 && t_k <= B;
+    if (in_range) inv_s[t_k - 1] = lane;
+    int cnt = 0;
+    for (int k = 0; k < B; ++k) cnt += __shfl(t_k, k, kWave) == lane + 1;
+    const bool bad = __ballot(lane < B && (cnt != 1 || !in_range)) != 0ull;
     if (bad) {
       if (lane == 0) {
         sh_L = -1;
         sh_stat = kDevBadTau;
       }
     } else {
+      const int kk = lane < B ? inv_s[lane] : 0;  // position with label lane + 1
+      const int x = __shfl(x_k, kk, kWave);
       bool acc = true;
       int stat = 0;
       if (lane < B) {
-        const int x = a.draft[static_cast<size_t>(s) * B + kk];
         float r;
         if (x < 0 || x >= V) {
           stat |= kDevBadToken;
@@ -135,7 +162,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   __syncthreads();
   const int L = sh_L;
   if (L < 0 || L == B) {
-    if (tid == 0) {
+    if (seg == 0 && tid == 0) {
       a.accept_len[s] = L < 0 ? 0 : B;
       a.correction[s] = -1;
       if (a.status && sh_stat) atomicOr(&a.status[s], sh_stat);
@@ -147,115 +174,123 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   const float* prow = a.p + (static_cast<size_t>(s) * B + kstar) * V;
   const float* qrow = a.q + (static_cast<size_t>(s) * B + kstar) * V;
   const bool vec = (V % 4) == 0;
-  const int per_wave = ((V + kAccWaves * kIter - 1) / (kAccWaves * kIter)) * kIter;
-  const int seg_lo = wave * per_wave;
-  const int seg_hi = min(V, seg_lo + per_wave);
-  const float u_corr = a.u[static_cast<size_t>(s) * (B + 1) + B];
 
+  // ---- every workgroup: residual mass of its segment, published coherently ----
+  float w[kPerThread];
+  load_masses(prow, qrow, seg * kSeg + kPerThread * tid, V, vec, false, w);
+  double mine;
+  block_excl_scan(thread_sum(w), &mine);
+  double* segsum = a.seg_sum + static_cast<size_t>(s) * nseg;
+  if (tid == 0)
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(segsum + seg),
+                       static_cast<unsigned long long>(__double_as_longlong(mine)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);  // the store is acknowledged before the counter moves
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(&a.counters[s], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = prev == nseg - 1;
+  }
+  __syncthreads();
+  if (!sh_last) return;
+
+  // ---- last workgroup: all masses at once, threshold, segment, rescan ----
   bool use_p = false;
   for (int mode = 0; mode < 2; ++mode) {
     use_p = mode == 1;
-    // Pass 1: residual mass of this wave's contiguous segment.
-    double running = 0.0;
-    for (int base = seg_lo; base < seg_hi; base += kIter) {
-      const int y = base + 4 * lane;
-      float w[4] = {0.f, 0.f, 0.f, 0.f};
-      if (y < seg_hi) masses(prow, qrow, y, seg_hi, vec, use_p, w);
-      const double ls = ((static_cast<double>(w[0]) + w[1]) + w[2]) + w[3];
-      const double incl = wave_incl_scan(ls, lane);
-      running += __shfl(incl, kWave - 1, kWave);
+    if (!use_p) {
+      for (int j = tid; j < nseg; j += kAccThreads)
+        sh_mass[j] = __longlong_as_double(static_cast<long long>(__hip_atomic_load(
+            reinterpret_cast<unsigned long long*>(segsum + j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+    } else {  // zero residual: the (rare) fallback draws from p; masses of p, all segments here
+      for (int j = 0; j < nseg; ++j) {
+        float wp[kPerThread];
+        load_masses(prow, qrow, j * kSeg + kPerThread * tid, V, vec, true, wp);
+        double m;
+        block_excl_scan(thread_sum(wp), &m);
+        if (tid == 0) sh_mass[j] = m;
+      }
     }
-    if (lane == 0) seg_sum[wave] = running;
     __syncthreads();
     if (tid == 0) {
       double Z = 0.0;
-      for (int w = 0; w < kAccWaves; ++w) Z += seg_sum[w];
-      sh_done = Z > 0.0;
+      for (int j = 0; j < nseg; ++j) Z += sh_mass[j];
       if (Z > 0.0) {
         const double T = static_cast<double>(u_corr) * Z;
-        double cum = 0.0;
-        int wstar = -1, lastpos = -1;
-        for (int w = 0; w < kAccWaves; ++w) {
-          if (seg_sum[w] > 0.0) lastpos = w;
-          if (wstar < 0 && cum + seg_sum[w] > T) {
-            wstar = w;
+        double cum = 0.0, cum_last = 0.0;
+        int pick = -1, lastpos = -1;
+        for (int j = 0; j < nseg; ++j) {
+          const double m = sh_mass[j];
+          if (m > 0.0) lastpos = j, cum_last = cum;
+          if (cum + m > T) {
+            pick = j;
             break;
           }
-          cum += seg_sum[w];
+          cum += m;
         }
-        if (wstar < 0) {  // rounding left T at or past the total
-          wstar = lastpos;
-          cum = 0.0;
-          for (int w = 0; w < wstar; ++w) cum += seg_sum[w];
+        if (pick < 0) {  // rounding left T at or past the total
+          pick = lastpos;
+          cum = cum_last;
         }
-        sh_wstar = wstar;
-        sh_T = T;
+        sh_seg = pick;
         sh_base = cum;
+        sh_T = T;
+      } else {
+        sh_seg = -2;
+        if (mode == 0) sh_stat |= kDevZeroResidual;
       }
-      if (mode == 0 && !(Z > 0.0)) sh_stat |= kDevZeroResidual;
     }
     __syncthreads();
-    if (sh_done) break;
-  }
-  if (!sh_done) {  // no mass at all: nothing can be drawn
-    if (tid == 0) {
-      a.accept_len[s] = L;
-      a.correction[s] = -1;
-      if (a.status && sh_stat) atomicOr(&a.status[s], sh_stat);
-    }
-    return;
+    if (sh_seg != -2) break;
   }
 
-  // Pass 2: the chosen wave rescans its segment for the first y with
-  // running mass > T (zero-mass tokens are never drawn).
-  if (wave == sh_wstar) {
-    const double T = sh_T;
-    double running = sh_base;
-    int pick = -1, lastpos = -1;
-    for (int base = seg_lo; base < seg_hi && pick < 0; base += kIter) {
-      const int y = base + 4 * lane;
-      float w[4] = {0.f, 0.f, 0.f, 0.f};
-      if (y < seg_hi) masses(prow, qrow, y, seg_hi, vec, use_p, w);
-      const double ls = ((static_cast<double>(w[0]) + w[1]) + w[2]) + w[3];
-      const double incl = wave_incl_scan(ls, lane);
-      double excl = __shfl_up(incl, 1, kWave);
-      if (lane == 0) excl = 0.0;
-      int hit = -1, lp = -1;
-      double c = 0.0;
+  if (tid == 0) sh_pick = 0x7fffffff;
+  __syncthreads();
+  const int j = sh_seg;  // < 0: no mass anywhere
+  if (j >= 0) {
+    const int y0 = j * kSeg + kPerThread * tid;
+    if (j != seg || use_p) load_masses(prow, qrow, y0, V, vec, use_p, w);
+    double total;
+    const double excl = block_excl_scan(thread_sum(w), &total);
+    const double T = sh_T, base = sh_base;
+    int hit = -1, lastpos = -1;
+    double run = 0.0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c += w[j];
-        if (w[j] > 0.0f) {
-          lp = y + j;
-          if (hit < 0 && running + (excl + c) > T) hit = y + j;
-        }
+    for (int e = 0; e < kPerThread; ++e) {
+      run += static_cast<double>(w[e]);
+      if (w[e] > 0.0f) {
+        lastpos = y0 + e;
+        if (hit < 0 && base + (excl + run) > T) hit = y0 + e;
       }
-      const unsigned long long hits = __ballot(hit >= 0);
-      if (hits) {
-        const int first = __ffsll(static_cast<long long>(hits)) - 1;
-        pick = __shfl(hit, first, kWave);
-      }
-      const unsigned long long lps = __ballot(lp >= 0);
-      if (lps) {
-        const int lastl = 63 - __clzll(static_cast<long long>(lps));
-        lastpos = __shfl(lp, lastl, kWave);
-      }
-      running += __shfl(incl, kWave - 1, kWave);
     }
-    if (lane == 0) sh_pick = pick >= 0 ? pick : lastpos;
+    if (hit >= 0) atomicMin(&sh_pick, hit);
+    __syncthreads();
+    const bool none = sh_pick == 0x7fffffff;
+    __syncthreads();
+    if (none) {  // rounding: no crossing inside the segment; take its last positive entry
+      if (tid == 0) sh_pick = -1;
+      __syncthreads();
+      if (lastpos >= 0) atomicMax(&sh_pick, lastpos);
+    }
+  } else if (tid == 0) {
+    sh_pick = -1;  // no mass at all: nothing can be drawn
   }
   __syncthreads();
   if (tid == 0) {
     a.accept_len[s] = L;
     a.correction[s] = sh_pick;
     if (a.status && sh_stat) atomicOr(&a.status[s], sh_stat);
+    __hip_atomic_store(&a.counters[s], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 }  // namespace
 
+int accept_segments(int V) { return (V + kSeg - 1) / kSeg; }
+
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_kernel, dim3(a.b), dim3(kAccThreads), 0, stream, a);
+  dim3 grid(static_cast<unsigned>(accept_segments(a.V)), static_cast<unsigned>(a.b));
+  hipLaunchKernelGGL(accept_kernel, grid, dim3(kAccThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -4,15 +4,18 @@
 // Decoding in Diffusion Language Models" and [fr] "SimSD: Simple Speculative
 // Decoding in Diffusion Language Models", Methodologie 3): the mask slot D~_k
 // takes the rotary position of its paired data token D_k. The kernel makes
-// that literal: one workgroup owns response position k of one sequence,
-// evaluates the d/2 rotation angles of that position once, and applies them
-// to the rows of both D_k and D~_k, for the query heads and the KV heads.
+// that literal: a workgroup owns response position k of one sequence (and a
+// chunk of heads), evaluates the d/2 rotation angles of that position once,
+// and applies the same angles to the rows of both D_k and D~_k, for query and
+// KV heads.
 //
-// Work per workgroup is tiny (2 rows x (Hq + Hkv) heads x d elements), so the
-// kernel is bound by HBM traffic (read + write of Q and K of the block); fp64
-// is used for angles, cos/sin and the rotation, and each output is rounded to
-// bf16 once.
+// The kernel is bound by latency and HBM traffic (one read + one write of the
+// block's Q and K); the head dimension of the grid gives every thread a single
+// rotation. fp64 is used for angles, cos/sin and the rotation, and each output
+// is rounded to bf16 once.
 #include "simsd_internal.h"
+
+#include <algorithm>
 
 namespace simsd {
 
@@ -63,7 +66,10 @@ __device__ __forceinline__ void rotate4(uint16_t* row, int i0, int half, bool in
   }
 }
 
-__global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a) {
+// Grid: (sequence, position k) x head chunks. Threads of a workgroup each own
+// one group of 4 pairs of one row (D_k or D~_k) of one head, so every thread
+// does a single independent load / rotate / store.
+__global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a, int heads_per_wg) {
   __shared__ double cs_d[kMaxHalf], sn_d[kMaxHalf];  // angles of D_k
   __shared__ double cs_t[kMaxHalf], sn_t[kMaxHalf];  // angles of D~_k (same unless no_copy)
   const int s = blockIdx.x / a.B;
@@ -76,18 +82,24 @@ __global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a) {
     const double inv_freq = pow(a.base, -2.0 * tid / a.d);
     double ang = static_cast<double>(pos_d) * inv_freq;
     sincos(ang, &sn_d[tid], &cs_d[tid]);
-    ang = static_cast<double>(pos_t) * inv_freq;
-    sincos(ang, &sn_t[tid], &cs_t[tid]);
+    if (a.no_copy) {
+      ang = static_cast<double>(pos_t) * inv_freq;
+      sincos(ang, &sn_t[tid], &cs_t[tid]);
+    }
   }
   __syncthreads();
-  // Work items: (row in {D_k, D~_k}) x (head in Q then K) x (groups of 4 pairs)
+  const double* cs = cs_d;
+  const double* sn = sn_d;
+  // items of this workgroup: (row slot, head in this chunk, group of 4 pairs)
   const int groups = half / 4;
   const int heads = a.Hq + a.Hkv;
-  const int items = 2 * heads * groups;
+  const int h0 = blockIdx.y * heads_per_wg;
+  const int nh = min(heads_per_wg, heads - h0);
+  const int items = 2 * nh * groups;
   for (int it = tid; it < items; it += kRopeThreads) {
     const int grp = it % groups;
-    const int hh = (it / groups) % heads;
-    const int slot = it / (groups * heads);  // 0: D_k, 1: D~_k
+    const int hh = h0 + (it / groups) % nh;
+    const int slot = it / (groups * nh);  // 0: D_k, 1: D~_k
     const int r = k + slot * a.B;
     uint16_t* row;
     if (hh < a.Hq) {
@@ -95,15 +107,21 @@ __global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a) {
     } else {
       row = a.k + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hkv + (hh - a.Hq)) * a.d;
     }
-    rotate4(row, grp * 4, half, a.interleaved != 0, slot ? cs_t : cs_d, slot ? sn_t : sn_d);
+    const bool use_t = slot && a.no_copy;
+    rotate4(row, grp * 4, half, a.interleaved != 0, use_t ? cs_t : cs, use_t ? sn_t : sn);
   }
 }
 
 }  // namespace
 
 hipError_t launch_rope_copy(const RopeArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(a.b) * static_cast<unsigned>(a.B));
-  hipLaunchKernelGGL(rope_copy_kernel, grid, dim3(kRopeThreads), 0, stream, a);
+  // one thread per (row slot, head, 4-pair group): 2 * groups items per head
+  const int groups = a.d / 8;
+  const int heads_per_wg = std::max(1, kRopeThreads / (2 * groups));
+  const int heads = a.Hq + a.Hkv;
+  dim3 grid(static_cast<unsigned>(a.b) * static_cast<unsigned>(a.B),
+            static_cast<unsigned>((heads + heads_per_wg - 1) / heads_per_wg));
+  hipLaunchKernelGGL(rope_copy_kernel, grid, dim3(kRopeThreads), 0, stream, a, heads_per_wg);
   return hipGetLastError();
 }
 

@@ -117,23 +117,31 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
 }
 
 size_t simsd_accept_workspace(int b, int B, int V) {
-  (void)b, (void)B, (void)V;
-  return 0;
+  if (b < 1 || b > simsd::kMaxSeqCounters || B < 1 || B > 64 || V < 1 || V > simsd::kMaxAcceptVocab)
+    return 0;
+  const size_t seg = static_cast<size_t>(b) * simsd::accept_segments(V) * sizeof(double);
+  return static_cast<size_t>(simsd::kMaxSeqCounters) * sizeof(int32_t) + (seg + 255) / 256 * 256;
 }
 
 int simsd_accept(const float* p, const float* q, const int32_t* draft_tokens, const int32_t* tau,
                  const float* uniforms, int b, int B, int V, int32_t* accept_len,
                  int32_t* correction_token, int32_t* status, void* workspace, size_t ws_bytes,
                  void* stream) {
-  (void)workspace, (void)ws_bytes;
   if (!p || !q || !draft_tokens || !tau || !uniforms || !accept_len || !correction_token)
     return SIMSD_ERR_NULL;
-  if (b < 1 || B < 1 || B > 64 || V < 1) return SIMSD_ERR_SIZE;
+  if (b < 1 || b > simsd::kMaxSeqCounters || B < 1 || B > 64 || V < 1 || V > simsd::kMaxAcceptVocab)
+    return SIMSD_ERR_SIZE;
   if (!aligned16(p) || !aligned16(q)) return SIMSD_ERR_ALIGN;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      ws_bytes < simsd_accept_workspace(b, B, V))
+    return SIMSD_ERR_WORKSPACE;
   simsd::AcceptArgs a{};
   a.p = p, a.q = q, a.draft = draft_tokens, a.tau = tau, a.u = uniforms;
   a.b = b, a.B = B, a.V = V;
   a.accept_len = accept_len, a.correction = correction_token, a.status = status;
+  a.counters = static_cast<int32_t*>(workspace);
+  a.seg_sum = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                        static_cast<size_t>(simsd::kMaxSeqCounters) * sizeof(int32_t));
   return launch_status(simsd::launch_accept(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -9,6 +9,7 @@
 namespace simsd {
 
 constexpr int kWave = 64;
+constexpr int kMaxSeqCounters = 65536;  // counter words at the start of a workspace
 
 // Extra device status bit (kept beside the public ones in simsd.h).
 constexpr int kDevBadTau = 1;
@@ -86,6 +87,7 @@ struct AttnArgs {
 
 struct AttnPlan {
   int nwc, qb;        // compute waves and 16-row query blocks per wave
+  int pipe;           // key-tile pipeline variant (keys per tile x ring stages)
   int rows_per_wg;
   int row_slices;
   int chunk, nsplit;
@@ -102,11 +104,17 @@ struct AcceptArgs {
   int32_t* accept_len;
   int32_t* correction;
   int32_t* status;
+  int32_t* counters;  // [b], zero between calls
+  double* seg_sum;    // [b][segments] residual mass per vocabulary segment
 };
+
+int accept_segments(int V);
+
+constexpr int kMaxAcceptVocab = 1 << 21;  // vocabulary entries per row the acceptance kernel takes
 
 constexpr int kAttnTileKeys = 64;  // keys staged per tile
 constexpr int kAttnThreads = 256;
-constexpr int kAttnMaxUnits = 65536;  // (sequence, KV head, row slice) units per call
+constexpr int kAttnMaxUnits = kMaxSeqCounters;  // (sequence, KV head, row slice) units per call
 
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule);
 

@@ -14,24 +14,27 @@
 //    head and all block rows form M = G * rows query rows, so every K/V byte
 //    fetched from HBM feeds M rows (grouped-query reuse). M is covered by up
 //    to 4 compute waves of 1-2 MFMA row blocks of 16.
-//  * The prefix is split into chunks of `chunk` keys (split-KV), one
-//    workgroup per (unit, chunk), so a long prefix fills all 256 CUs. The
-//    block keys (2B <= 128) are taken by the workgroup of chunk 0 after its
-//    prefix keys, with the temporal mask generated from tau held in LDS.
-//  * Key tiles of 64 keys are streamed HBM -> registers (16-byte loads, one
-//    tile of prefetch ahead) -> LDS. K is stored row-major; V is stored
-//    transposed with an XOR-swizzled key column so the PV operand is one
-//    16-byte LDS read and the transposing writes do not collide on banks.
+//  * The prefix is split into chunks (split-KV), about one workgroup per CU,
+//    so a long prefix fills all 256 CUs. The block keys (2B <= 128) are taken
+//    by the workgroup of chunk 0 after its prefix keys, with the temporal mask
+//    generated from tau held in LDS.
+//  * Key tiles stream HBM -> LDS with global_load_lds_dwordx4 (no register
+//    staging) into a ring of NS tiles; NS - 1 tiles are in flight while one is
+//    consumed, with one barrier per tile. K and V stay row-major in LDS with
+//    XOR-swizzled 16-byte chunks so that the K operand reads and the
+//    transposing V reads (ds_read_b64_tr_b16, which yields the V^T operand
+//    from row-major V) hit distinct banks.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32
 //    accumulation. The S^T output layout puts 8 consecutive keys of one query
 //    in each lane, which is exactly the P^T operand of the PV product, so the
-//    softmax never leaves registers. Row maxima need two cross-lane steps;
-//    row sums stay lane-local until the end.
-//  * Split partials (m, l, unnormalised O) go to the workspace in register
-//    order; the last workgroup of a unit to finish (agent-scope counter)
-//    merges them with the log-sum-exp rule and writes the output, then resets
-//    the counter. Workgroup ids are remapped so that the chunks of one unit
-//    run on the same XCD (ids are dispatched round-robin over the 8 XCDs).
+//    softmax never leaves registers. Row maxima and sums over the 4 lanes of a
+//    query use lane swaps; O is rescaled only when a row maximum moved.
+//  * Split partials (m, l, unnormalised O) are handed to the last workgroup
+//    of the unit to finish through device-coherent 16-byte stores / loads and
+//    an agent-scope counter (no cache-wide fences); it merges them with the
+//    log-sum-exp rule, writes the output and resets the counter. Workgroup ids
+//    are remapped so the chunks of one unit run on the same XCD (ids are
+//    dispatched round-robin over the 8 XCDs).
 #include "simsd_internal.h"
 
 #include <algorithm>
@@ -42,18 +45,16 @@ namespace simsd {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define SIMSD_LDS __attribute__((address_space(3)))
 
-constexpr int TK = kAttnTileKeys;
 constexpr float kLn2 = 0.6931471805599453f;
-
-template <int D>
-struct AttnSmem {
-  uint16_t k[TK][D + 8];   // key tile, row-major, 16-byte row pad
-  uint16_t vt[D][TK + 8];  // value tile transposed; key column XOR (4 * (d / 8))
-  int tau[64];
-  int last;
-};
+constexpr int TK = kAttnTileKeys;  // chunk granularity of the split plan
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   union {
@@ -65,33 +66,112 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  union {
+    bf16x2 b;
+    uint32_t u;
+  } c;
+  c.b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);  // v_cvt_pk_bf16_f32, nearest even
+  return c.u;
 }
 
-// Temporal mask between block rows (query row qr with slot flag / label, key
-// block row c). See the header comment for the rule.
+// 16 bytes HBM -> LDS without passing through registers (global_load_lds_dwordx4,
+// scalar-base form): lane l reads sbase + voff and its bytes land at LDS byte
+// address m0 + 16 * l; `sbase` and `lds` are wave-uniform. Issued as inline asm
+// so that the compiler does not add its own (conservative) wait before later
+// LDS reads; the kernel waits explicitly with vmcnt.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer descriptor over [base, base + bytes) for device-coherent (sc1) 8- and
+// 16-byte accesses: partials written by one workgroup are read by another,
+// possibly on another XCD, without cache-wide writeback or invalidation.
+constexpr int kCoherent = 16;  // cache-policy bit selecting sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+
+// Max / sum of x over lanes l, l^16, l^32, l^48 (the four lanes holding one
+// query row) with the VALU lane-swap instructions instead of LDS permutes.
+__device__ __forceinline__ float max_over_row_lanes(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_row_lanes(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0) only
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// XOR swizzles of the 16-byte chunks inside a key row of a staged tile. A K
+// operand read (16 lanes, rows 8(n/4) + n%4, one chunk column) and a V operand
+// transposing read (32 lanes, 8 rows x 32 bytes) then touch distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return (row & 3) | (((row >> 3) & 3) << 2);
+  else return ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return ((row & 3) | (((row >> 3) & 1) << 2)) << 1;
+  else return (((row >> 1) & 1) | (((row >> 3) & 1) << 1)) << 1;
+}
+
+// Temporal mask between block rows, branch-free: query with slot flag / label,
+// key block row c in [0, 2B) (c < B: data token D_{c+1}; else mask slot
+// D~_{c-B+1}).
 __device__ __forceinline__ bool block_allowed(bool q_slot, int tau_q, int c, int B,
                                               const int* tau_s, int data_rule) {
   const bool k_slot = c >= B;
   const int tau_k = tau_s[k_slot ? c - B : c];
-  if (q_slot) return k_slot ? (tau_k >= tau_q) : (tau_k < tau_q);
-  if (k_slot) return false;
-  return data_rule == 1 ? true : (tau_k <= tau_q);
+  const bool slot_row = k_slot ? (tau_k >= tau_q) : (tau_k < tau_q);
+  const bool data_row = !k_slot && (data_rule == 1 || tau_k <= tau_q);
+  return q_slot ? slot_row : data_row;
 }
 
-template <int D, int NWC, int QB, bool OUT_F32>
+// D head dim; NWC compute waves x QB 16-row query blocks; TK keys per staged
+// tile; NS tiles in the LDS ring (NS - 1 in flight while one is consumed).
+template <int D, int NWC, int QB, int TKEYS, int NS, bool OUT_F32>
 __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
-  constexpr int KK = D / 32;                        // MFMA k-steps of Q.K
-  constexpr int DB = D / 16;                        // 16-wide d blocks of P.V
-  constexpr int CH = D / 8;                         // 16-byte chunks per row
-  constexpr int CPT = TK * CH / kAttnThreads;       // chunks per thread per tensor
-  constexpr int MWG = NWC * QB * 16;                // query rows per workgroup
-  static_assert(CPT >= 1 && TK * CH % kAttnThreads == 0, "tile/thread mismatch");
-  static_assert(NWC >= 1 && NWC <= 4, "compute waves");
+  constexpr int TK = TKEYS;         // keys per staged tile
+  constexpr int KK = D / 32;          // MFMA k-steps of Q.K
+  constexpr int DB = D / 16;          // 16-wide d blocks of P.V
+  constexpr int CH = D / 8;           // 16-byte chunks per key row
+  constexpr int ROW_B = D * 2;        // bytes per key row
+  constexpr int RPI = 1024 / ROW_B;   // key rows per DMA wave instruction
+  constexpr int IPW = TK / RPI / 4;   // DMA instructions per wave per tensor per tile
+  constexpr int DPW = 2 * IPW;        // ... for K and V together
+  constexpr int TENSOR_B = TK * ROW_B;
+  constexpr int STAGE_B = 2 * TENSOR_B;
+  constexpr int NSUB = TK / 32;       // 32-key PV steps per tile
+  constexpr int NKB = TK / 16;        // 16-key S^T blocks per tile
+  constexpr int MWG = NWC * QB * 16;  // query rows per workgroup
+  static_assert(IPW >= 1 && (TK / RPI) % 4 == 0, "tile / wave mismatch");
+  static_assert(NS >= 2 && (NS - 2) * DPW < 64, "pipeline depth");
 
-  __shared__ AttnSmem<D> sm;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE_B];
+  __shared__ int tau_s[64];
+  __shared__ int last_s;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps DMA math scalar
   const int a16 = lane >> 4, n16 = lane & 15;
 
   // ---- which (sequence, KV head, row slice, split) this workgroup owns ----
@@ -112,15 +192,71 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   if (split >= ns) return;
   const int key_lo = split * a.chunk;
   const int key_hi = min(P, key_lo + a.chunk);
-  const bool with_block = split == 0;
 
-  if (tid < 64) sm.tau[tid] = tid < B ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
-  __syncthreads();
+  if (tid < 64) tau_s[tid] = tid < B ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
 
+  // ---- tile schedule: prefix tiles of this chunk, then (split 0) the block ----
+  const uint32_t rsb = static_cast<uint32_t>(a.Hkv) * ROW_B;  // bytes between key rows
+  const char* kpre = reinterpret_cast<const char*>(a.k_pre + (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D);
+  const char* vpre = reinterpret_cast<const char*>(a.v_pre + (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D);
+  const char* kblk = reinterpret_cast<const char*>(a.k_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D);
+  const char* vblk = reinterpret_cast<const char*>(a.v_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D);
+  const int n_pre = (key_hi - key_lo + TK - 1) / TK;
+  const int ntiles = n_pre + (split == 0 ? (twoB + TK - 1) / TK : 0);
+  SIMSD_LDS uint8_t* const ring_l = (SIMSD_LDS uint8_t*)ring;
+  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_l));
+
+  // Per-lane byte offsets of the DMA of a full tile: instruction i of this wave
+  // fills LDS rows gi*RPI .. gi*RPI+RPI-1 (gi = 4i + wave); lane l supplies the
+  // chunk that the swizzle places in LDS slot l % CH of its row.
+  uint32_t koff[IPW], voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int row = (i * 4 + wave) * RPI + lane / CH;
+    const int p = lane % CH;
+    koff[i] = static_cast<uint32_t>(row) * rsb + 16u * static_cast<uint32_t>(p ^ swz_k<D>(row));
+    voff[i] = static_cast<uint32_t>(row) * rsb + 16u * static_cast<uint32_t>(p ^ swz_v<D>(row));
+  }
+
+  // Issue the DMA of tile t into ring slot t % NS. In a partial tile, rows past
+  // the valid end re-read the last valid row (in bounds; those keys are masked).
+  auto issue = [&](int t) {
+    const bool blk = t >= n_pre;
+    const int r0 = blk ? (t - n_pre) * TK : key_lo + t * TK;
+    const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
+    const char* kb = (blk ? kblk : kpre) + static_cast<size_t>(r0) * rsb;
+    const char* vb = (blk ? vblk : vpre) + static_cast<size_t>(r0) * rsb;
+    const uint32_t stage = ring_base + static_cast<uint32_t>((t % NS) * STAGE_B);
+    if (nvalid == TK) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const uint32_t lds = stage + static_cast<uint32_t>((i * 4 + wave) * 1024);
+        dma16(kb, koff[i], lds);
+        dma16(vb, voff[i], lds + TENSOR_B);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int row = (i * 4 + wave) * RPI + lane / CH;
+        const int p = lane % CH;
+        const uint32_t src = static_cast<uint32_t>(min(row, nvalid - 1)) * rsb;
+        const uint32_t lds = stage + static_cast<uint32_t>((i * 4 + wave) * 1024);
+        dma16(kb, src + 16u * static_cast<uint32_t>(p ^ swz_k<D>(row)), lds);
+        dma16(vb, src + 16u * static_cast<uint32_t>(p ^ swz_v<D>(row)), lds + TENSOR_B);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) issue(t);
+
+  wait_lgkm0();
+  block_barrier();  // tau_s visible (the DMA above is not waited for here)
   if (a.status && split == 0 && slice == 0 && g == 0 && wave == 0) {
     int cnt = 0;
     if (lane < B)
-      for (int k = 0; k < B; ++k) cnt += sm.tau[k] == lane + 1;
+      for (int k = 0; k < B; ++k) cnt += tau_s[k] == lane + 1;
     const bool bad_tau = __ballot(lane < B && cnt != 1) != 0ull;
     if (lane == 0 && (bad_tau || bad_prefix))
       atomicOr(&a.status[s], (bad_tau ? kDevBadTau : 0) | (bad_prefix ? kDevBadPrefix : 0));
@@ -145,11 +281,18 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
       qreg[qb][kk] = as_bf16x8(v);
     }
     slot_q[qb] = r >= B;
-    tau_q[qb] = sm.tau[r >= B ? r - B : r];
+    tau_q[qb] = tau_s[r >= B ? r - B : r];
   }
+  // Make the compiler complete the Q loads here, not at their first use inside
+  // the tile loop (a wait there would also drain the DMA ring every tile).
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qreg[qb][kk]));
 
+  const float c2 = a.scale_log2;  // softmax scale * log2(e)
   f32x4 oacc[QB][DB];
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[QB];  // running max of raw scores, lane-partial sums
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
@@ -158,190 +301,201 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- tile schedule: prefix tiles of this chunk, then the block tiles ----
-  const size_t row_stride = static_cast<size_t>(a.Hkv) * D;
-  const uint16_t* kpre = a.k_pre + (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D;
-  const uint16_t* vpre = a.v_pre + (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D;
-  const uint16_t* kblk = a.k_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D;
-  const uint16_t* vblk = a.v_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D;
-  const int n_pre = (key_hi - key_lo + TK - 1) / TK;
-  const int n_blk = with_block ? (twoB + TK - 1) / TK : 0;
-  const int ntiles = n_pre + n_blk;
-
-  uint4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int t) {
-    const bool blk = t >= n_pre;
-    const int r0 = blk ? (t - n_pre) * TK : key_lo + t * TK;
-    const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
-    const uint16_t* kb = blk ? kblk : kpre;
-    const uint16_t* vb = blk ? vblk : vpre;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + kAttnThreads * i;
-      const int j = c / CH, cc = c % CH;
-      if (j < nvalid) {
-        const size_t off = static_cast<size_t>(r0 + j) * row_stride + cc * 8;
-        kreg[i] = *reinterpret_cast<const uint4*>(kb + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(vb + off);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);  // zero keys/values: no NaN from stale LDS
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + kAttnThreads * i;
-      const int j = c / CH, cc = c % CH;
-      *reinterpret_cast<uint4*>(&sm.k[j][cc * 8]) = kreg[i];
-      const int jp = j ^ (4 * cc);
-      const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.vt[cc * 8 + 2 * e][jp] = static_cast<uint16_t>(w[e]);
-        sm.vt[cc * 8 + 2 * e + 1][jp] = static_cast<uint16_t>(w[e] >> 16);
-      }
-    }
-  };
-
-  if (ntiles > 0) load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+    // tile t must have landed; tiles t+1 .. t+NS-2 may still be in flight
+    const int ahead = min(NS - 2, ntiles - 1 - t);
+    if constexpr (NS >= 4) {
+      if (ahead >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * DPW>();
+      else if (ahead == 1) wait_vmcnt<DPW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NS == 3) {
+      if (ahead >= 1) wait_vmcnt<DPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();  // every wave's share of tile t is in LDS; tile t-1 is consumed
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
     if (!computes) continue;
 
     const bool blk = t >= n_pre;
     const int r0 = blk ? (t - n_pre) * TK : key_lo + t * TK;
     const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
+    SIMSD_LDS uint8_t* const kst_p = ring_l + (t % NS) * STAGE_B;
+    SIMSD_LDS uint8_t* const vst_p = kst_p + TENSOR_B;
+
+    // S^T blocks: block kb covers keys 32(kb/2) + 8(m/4) + 4(kb%2) + m%4 for MFMA row m,
+    // so lane (a16, n16) ends up with keys 32ks + 8*a16 + 0..7 of query n16.
+    f32x4 sacc[QB][NKB];
 #pragma unroll
-    for (int ks = 0; ks < TK / 32; ++ks) {
-      if (32 * ks >= nvalid) break;
-      // S^T block kb: MFMA row mr -> key 32ks + 8(mr/4) + 4kb + mr%4
-      f32x4 sacc[QB][2];
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int row = 32 * (kb >> 1) + 8 * (n16 >> 2) + 4 * (kb & 1) + (n16 & 3);
+      const int sw = swz_k<D>(row);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key_m = 32 * ks + 8 * (n16 >> 2) + 4 * kb + (n16 & 3);
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[key_m][32 * kk + 8 * a16]));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[qb][kk], sacc[qb][kb], 0, 0, 0);
-        }
-      }
-      // lane holds keys 32ks + 8*a16 + (4kb + i) of query n16
-      bf16x8 pop[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float sv[8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kl = 32 * ks + 8 * a16 + 4 * kb + i;
-            bool ok = kl < nvalid;
-            if (blk && ok) ok = block_allowed(slot_q[qb], tau_q[qb], r0 + kl, B, sm.tau, a.data_rule);
-            sv[4 * kb + i] = ok ? sacc[qb][kb][i] * a.scale_log2 : -INFINITY;
-          }
-        float mx = sv[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-        m_run[qb] = m_new;
-        uint32_t pk[4];
-        float psum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(sv[2 * j] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(sv[2 * j + 1] - m_use);
-          pk[j] = pack_bf16x2(p0, p1);
-          psum += bf16_to_f32(static_cast<uint16_t>(pk[j])) + bf16_to_f32(static_cast<uint16_t>(pk[j] >> 16));
-        }
-        l_run[qb] = l_run[qb] * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-        pop[qb] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-      }
-      // O^T += V^T P^T: operand = 8 consecutive keys of column d
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + n16;
-        const int pb = (4 * ks + a16) ^ db;
-        uint4 raw = *reinterpret_cast<const uint4*>(&sm.vt[d][8 * pb]);
-        if (n16 & 8) raw = make_uint4(raw.z, raw.w, raw.x, raw.y);  // halves swapped by the swizzle
-        const bf16x8 av = as_bf16x8(raw);
+      for (int kk = 0; kk < KK; ++kk) {
+        union {
+          u32x4 u;
+          bf16x8 b;
+        } ak;
+        ak.u = *reinterpret_cast<SIMSD_LDS const u32x4*>(kst_p + row * ROW_B + 16 * ((4 * kk + a16) ^ sw));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pop[qb], oacc[qb][db], 0, 0, 0);
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak.b, qreg[qb][kk], sacc[qb][kb], 0, 0, 0);
       }
     }
+
+    const bool need_mask = blk || nvalid < TK;
+    bf16x8 pop[QB][NSUB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kl = 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
+            bool ok = kl < nvalid;
+            if (blk && ok) ok = block_allowed(slot_q[qb], tau_q[qb], r0 + kl, B, tau_s, a.data_rule);
+            if (!ok) sacc[qb][kb][i] = -INFINITY;
+          }
+      }
+      float mx = sacc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[qb][kb][i]);
+      mx = max_over_row_lanes(mx);
+      const float m_new = fmaxf(m_run[qb], mx);
+      const bool grew = m_new > m_run[qb];
+      if (__ballot(grew) != 0ull) {  // rescale only when some row max moved
+        const float alpha = grew ? __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c2) : 1.0f;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float nmc = m_new == -INFINITY ? 0.0f : -m_new * c2;
+      float psum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NSUB; ++ks) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const f32x4 sv = sacc[qb][2 * ks + kb2];
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[0], c2, nmc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[1], c2, nmc));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2], c2, nmc));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[3], c2, nmc));
+          psum += (p0 + p1) + (p2 + p3);
+          pk[2 * kb2] = pack_bf16x2(p0, p1);
+          pk[2 * kb2 + 1] = pack_bf16x2(p2, p3);
+        }
+        pop[qb][ks] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      }
+      l_run[qb] += psum;
+    }
+
+    // O^T += V^T P^T; the V^T operand (8 consecutive keys of one d column) comes
+    // from two transposing LDS reads of the row-major, swizzled V tile.
+#pragma unroll
+    for (int ks = 0; ks < NSUB; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        i16x4 part[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 32 * ks + 8 * a16 + 4 * hh + (n16 >> 2);
+          const int c = 2 * db + ((n16 & 3) >> 1);
+          part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<SIMSD_LDS i16x4*>(
+              vst_p + row * ROW_B + 16 * (c ^ swz_v<D>(row)) + 8 * (n16 & 1)));
+        }
+        union {
+          i16x4 h[2];
+          bf16x8 b;
+        } av;
+        av.h[0] = part[0];
+        av.h[1] = part[1];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.b, pop[qb][ks], oacc[qb][db], 0, 0, 0);
+      }
   }
 
   // ---- finish: full row sums, then either write or hand off to the merge ----
-  float l_tot[QB];
+  float l_tot[QB], m_sc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    l_tot[qb] = l;
+    l_tot[qb] = sum_over_row_lanes(l_run[qb]);
+    m_sc[qb] = m_run[qb] * c2;  // log2 units
   }
 
   if (ns > 1) {
+    // Hand the split's partial (m, l, unnormalised O) to the last workgroup of
+    // the unit. Partials are written and read with device-coherent (agent
+    // scope) accesses, so no cache-wide writeback/invalidate is needed; the
+    // barrier waits for this workgroup's stores to be acknowledged before the
+    // counter is bumped, and the last workgroup reads only after its bump
+    // returned.
+    constexpr int PART_O_B = NWC * QB * DB * 64 * 16;  // bytes of one split's O partial
+    constexpr int PART_ML_B = MWG * 8;                  // bytes of one split's (m, l) pairs
     const size_t part = static_cast<size_t>(us) * a.nsplit + split;
     if (computes) {
-      f32x4* po = reinterpret_cast<f32x4*>(a.part_o) + part * (NWC * QB * DB * 64);
+      const auto ro = coherent_rsrc(reinterpret_cast<char*>(a.part_o) + part * PART_O_B, PART_O_B);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) po[((wave * QB + qb) * DB + db) * 64 + lane] = oacc[qb][db];
+        for (int db = 0; db < DB; ++db)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[qb][db]), ro,
+                                                 (((wave * QB + qb) * DB + db) * 64 + lane) * 16, 0, kCoherent);
       if (a16 == 0) {
-        float2* pml = reinterpret_cast<float2*>(a.part_ml) + part * MWG;
+        const auto rml = coherent_rsrc(reinterpret_cast<char*>(a.part_ml) + part * PART_ML_B, PART_ML_B);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) pml[(wave * QB + qb) * 16 + n16] = make_float2(m_run[qb], l_tot[qb]);
+        for (int qb = 0; qb < QB; ++qb)
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(u32x2, f32x2{m_sc[qb], l_tot[qb]}), rml, ((wave * QB + qb) * 16 + n16) * 8, 0,
+              kCoherent);
       }
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
     __syncthreads();
     if (tid == 0) {
-      const int prev = __hip_atomic_fetch_add(&a.counters[us], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      sm.last = prev == ns - 1;
+      const int prev = __hip_atomic_fetch_add(&a.counters[us], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_s = prev == ns - 1;
     }
     __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
+    if (!last_s) return;
     if (computes) {
       const size_t part0 = static_cast<size_t>(us) * a.nsplit;
+      const auto ro = coherent_rsrc(reinterpret_cast<char*>(a.part_o) + part0 * PART_O_B, ns * PART_O_B);
+      const auto rml = coherent_rsrc(reinterpret_cast<char*>(a.part_ml) + part0 * PART_ML_B, ns * PART_ML_B);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int row = (wave * QB + qb) * 16 + n16;
         float mmax = -INFINITY;
         for (int k = 0; k < ns; ++k) {
-          const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[(part0 + k) * MWG + row];
-          mmax = fmaxf(mmax, ml.x);
+          const f32x2 ml = __builtin_bit_cast(
+              f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, k * PART_ML_B + row * 8, 0, kCoherent));
+          mmax = fmaxf(mmax, ml[0]);
         }
         const float m_use = mmax == -INFINITY ? 0.0f : mmax;
         float lsum = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int k = 0; k < ns; ++k) {
-          const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[(part0 + k) * MWG + row];
-          const float w = __builtin_amdgcn_exp2f(ml.x - m_use);
-          lsum += w * ml.y;
-          const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + (part0 + k) * (NWC * QB * DB * 64);
+          const f32x2 ml = __builtin_bit_cast(
+              f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, k * PART_ML_B + row * 8, 0, kCoherent));
+          const float w = __builtin_amdgcn_exp2f(ml[0] - m_use);
+          lsum += w * ml[1];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[qb][db] += w * po[((wave * QB + qb) * DB + db) * 64 + lane];
+          for (int db = 0; db < DB; ++db)
+            oacc[qb][db] += w * __builtin_bit_cast(
+                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ro, k * PART_O_B + (((wave * QB + qb) * DB + db) * 64 + lane) * 16,
+                                               0, kCoherent));
         }
-        m_run[qb] = mmax;
+        m_sc[qb] = mmax;
         l_tot[qb] = lsum;
       }
     }
@@ -370,26 +524,34 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow * D + d0) = v;
       }
     }
-    if (a.lse && a16 == 0) a.lse[orow] = (m_run[qb] + __log2f(l_tot[qb])) * kLn2;
+    if (a.lse && a16 == 0) a.lse[orow] = (m_sc[qb] + __log2f(l_tot[qb])) * kLn2;
   }
 }
 
-template <int D, int NWC, int QB>
+template <int D, int NWC, int QB, int TK, int NS>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(a.total_grid)), block(kAttnThreads);
   if (a.out_f32)
-    hipLaunchKernelGGL((verify_attn_kernel<D, NWC, QB, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NWC, QB, TK, NS, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((verify_attn_kernel<D, NWC, QB, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NWC, QB, TK, NS, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
-  if (p.nwc == 1) return launch_variant<D, 1, 1>(a, stream);
-  if (p.nwc == 2) return launch_variant<D, 2, 1>(a, stream);
-  if (p.qb == 1) return launch_variant<D, 4, 1>(a, stream);
-  return launch_variant<D, 4, 2>(a, stream);
+  if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2>(a, stream);
+  if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2>(a, stream);
+  if (p.qb == 2) return launch_variant<D, 4, 2, 64, 2>(a, stream);
+  if constexpr (D == 128) {
+    switch (p.pipe) {
+      case 1: return launch_variant<D, 4, 1, 64, 2>(a, stream);
+      case 2: return launch_variant<D, 4, 1, 64, 3>(a, stream);
+      case 3: return launch_variant<D, 4, 1, 32, 3>(a, stream);
+      default: return launch_variant<D, 4, 1, 32, 4>(a, stream);
+    }
+  }
+  return launch_variant<D, 4, 1, 64, 2>(a, stream);
 }
 
 int env_int(const char* name, int dflt) {
@@ -419,8 +581,13 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
     p.nwc = 4, p.qb = 2;
   }
   p.rows_per_wg = p.nwc * p.qb * 16;
+  // tuning override of the key-tile ring (keys per tile x stages) for d = 128,
+  // 4 x 16 rows: 0 = 32x4 (default), 1 = 64x2, 2 = 64x3, 3 = 32x3
+  p.pipe = env_int("SIMSD_ATTN_PIPE", 0);
   p.row_slices = (M + p.rows_per_wg - 1) / p.rows_per_wg;
-  const int target = std::max(1, env_int("SIMSD_ATTN_TARGET_WG", 512));
+  // About one workgroup per CU: each workgroup pays a pipeline fill and a
+  // partial hand-off, so fewer, longer workgroups win once all CUs are busy.
+  const int target = std::max(1, env_int("SIMSD_ATTN_TARGET_WG", 256));
   const int chunk_max = std::max(TK, env_int("SIMSD_ATTN_CHUNK_MAX", 2048) / TK * TK);
   const long units = static_cast<long>(b) * Hkv * p.row_slices;
   const int max_tiles = std::max(1, (max_prefix + TK - 1) / TK);

@@ -82,7 +82,11 @@ def test_workspace_sizes(lib):
                 (1, 4, 1, 1, 64, 32), (1, 64, 32, 8, 128, 100)]:
         n = lib.simsd_verify_attention_workspace(*cfg)
         assert n % 256 == 0 and 0 < n < (1 << 31)
-    assert lib.simsd_accept_workspace(16, 8, 32768) == 0
+    n = lib.simsd_accept_workspace(16, 8, 32768)
+    assert n >= 262144 + 16 * 8 * 8 and n % 256 == 0
+    assert lib.simsd_accept_workspace(0, 8, 32768) == 0
+    assert lib.simsd_accept_workspace(1, 65, 32768) == 0
+    assert lib.simsd_accept_workspace(1, 8, 0) == 0
 
 
 def test_rope_host_errors(lib):
@@ -104,10 +108,15 @@ def test_rope_host_errors(lib):
 def test_accept_host_errors(lib):
     f = lambda **kw: lib.simsd_accept(kw.get("p", FAKE), kw.get("q", FAKE), FAKE, FAKE, FAKE,
                                       kw.get("b", 1), kw.get("B", 4), kw.get("V", 16),
-                                      kw.get("L", FAKE), FAKE, None, None, 0, None)
+                                      kw.get("L", FAKE), FAKE, None, kw.get("ws", FAKE),
+                                      kw.get("wsb", 1 << 30), None)
     assert f(p=None) == 1
     assert f(L=None) == 1
     assert f(b=0) == 2
     assert f(B=65) == 2
     assert f(V=0) == 2
+    assert f(V=(1 << 21) + 1) == 2
     assert f(q=MISALIGNED) == 7
+    assert f(ws=None) == 6
+    assert f(ws=MISALIGNED) == 6
+    assert f(wsb=lib.simsd_accept_workspace(1, 4, 16) - 1) == 6
