@@ -183,7 +183,11 @@ def main():
     max_prefix = max(lens)
     log(f"workload {WORKLOAD}: {w.describe()}")
 
+    # The prefix cache is stored head-major ([Hkv][sum P][d], SIMSD_KV_HEAD_MAJOR):
+    # each (sequence, KV head) split then streams one contiguous strip.
     base = {k: v.to(dev) for k, v in x.items() if torch.is_tensor(v)}
+    for key in ("k_pre", "v_pre"):
+        base[key] = base[key].transpose(0, 1).contiguous()
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.sets - 1)]
     b, B, Hq, Hkv, d = w.b, w.B, w.Hq, w.Hkv, w.d
     outs = [torch.empty_like(s["q_blk"]) for s in sets]
@@ -204,7 +208,8 @@ def main():
                 ctypes.c_float(w.rope_base), 0, hs)
         attn = (P(s["q_blk"]), P(s["k_blk"]), P(s["v_blk"]), P(s["k_pre"]), P(s["v_pre"]),
                 P(s["prefix_offsets"]), P(s["tau"]), P(outs[j]), None, b, B, Hq, Hkv, d,
-                max_prefix, ctypes.c_float(0.0), 0, None, P(ws), ws.numel(), hs)
+                max_prefix, ctypes.c_float(0.0), binding.SIMSD_KV_HEAD_MAJOR, None, P(ws),
+                ws.numel(), hs)
         acc = (P(s["p"]), P(s["q"]), P(s["draft"]), P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]),
                P(Cs[j]), None, P(ws_acc), ws_acc.numel(), hs)
         calls.append((rope, attn, acc))
@@ -280,6 +285,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{WORKLOAD}: {w.describe()}", "global_batch": b,
                    "prefix": max_prefix, "block_B": B, "input_sets_rotated": args.sets,
+                   "kv_cache_layout": "head-major [Hkv][sum P][d]",
                    "step": "rope_copy + verify_attention + accept"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

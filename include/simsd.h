@@ -71,11 +71,12 @@ typedef enum {
 #define SIMSD_ROPE_INTERLEAVED 1u /* pairing (2i, 2i+1) */
 #define SIMSD_ROPE_NO_COPY 2u     /* ablation: D~_k at start + B + k - 1 instead of start + k - 1 */
 
-/* simsd_verify_attention flags: data-row rule (2 bits) | output dtype */
+/* simsd_verify_attention flags: data-row rule (2 bits) | output dtype | cache layout */
 #define SIMSD_DATA_CAUSAL 0u /* D_i sees the prefix and D_j with tau(j) <= tau(i) (default) */
 #define SIMSD_DATA_BIDIR 1u  /* D_i sees the prefix and every D_j */
 #define SIMSD_DATA_SKIP 2u   /* data rows are not computed; their out/lse rows are untouched */
 #define SIMSD_OUT_F32 4u     /* out is fp32 instead of bf16 */
+#define SIMSD_KV_HEAD_MAJOR 8u /* k_pre / v_pre are [Hkv][sum P][d] instead of [sum P][Hkv][d] */
 
 /*
  * simsd_rope_copy -- rotary position embedding of the block's queries and
@@ -116,8 +117,13 @@ int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, i
  * maximum nor the sum) of scale * q.k, applied to the values.
  *
  *   q_blk, k_blk, v_blk  bf16 [b][2B][Hq|Hkv|Hkv][d] (post-RoPE)
- *   k_pre, v_pre         bf16 [sum_s P_s][Hkv][d]: packed prefix cache, rows
- *                        prefix_offsets[s] .. prefix_offsets[s+1]-1 belong to s
+ *   k_pre, v_pre         bf16 packed prefix cache, token-major [sum_s P_s][Hkv][d]
+ *                        (default) or, with SIMSD_KV_HEAD_MAJOR, head-major
+ *                        [Hkv][sum_s P_s][d]; rows prefix_offsets[s] ..
+ *                        prefix_offsets[s+1]-1 belong to sequence s. Head-major
+ *                        lets each KV head's keys stream contiguously (faster
+ *                        on long prefixes); sum_s P_s is read from
+ *                        prefix_offsets[b].
  *   prefix_offsets       int32 [b+1], non-decreasing, offsets[0] = 0
  *   tau                  int32 [b][B]
  *   out                  [b][2B][Hq][d], bf16 (or fp32 with SIMSD_OUT_F32)

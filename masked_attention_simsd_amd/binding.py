@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG, "libsimsd.so")
 # flag and status values, as in include/simsd.h
 SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY = 0, 1, 2
 SIMSD_DATA_CAUSAL, SIMSD_DATA_BIDIR, SIMSD_DATA_SKIP, SIMSD_OUT_F32 = 0, 1, 2, 4
+SIMSD_KV_HEAD_MAJOR = 8
 SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
 SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX = 8, 16
 
@@ -156,6 +157,8 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
                            flags: int = 0, status=None, workspace=None, stream=None):
     """Verify attention. Returns out ([b][2B][Hq][d], bf16 or fp32 with SIMSD_OUT_F32).
 
+    k_pre / v_pre are [sum P][Hkv][d], or [Hkv][sum P][d] with SIMSD_KV_HEAD_MAJOR.
+
     max_prefix: host int >= every prefix length; if None it is read back from
     prefix_offsets (a device-to-host copy, so not for timed loops).
     """
@@ -168,8 +171,10 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
     b, twoB, Hq, d = q_blk.shape
     B = twoB // 2
     Hkv = k_blk.shape[2]
+    head_major = bool(flags & SIMSD_KV_HEAD_MAJOR)
+    pre_ok = (k_pre.shape[0] == Hkv and k_pre.shape[2] == d) if head_major else k_pre.shape[1:] == (Hkv, d)
     if (twoB % 2 or tuple(k_blk.shape) != (b, twoB, Hkv, d) or tuple(v_blk.shape) != (b, twoB, Hkv, d)
-            or k_pre.shape[1:] != (Hkv, d) or v_pre.shape != k_pre.shape
+            or not pre_ok or v_pre.shape != k_pre.shape
             or prefix_offsets.shape[0] != b + 1 or tuple(tau.shape) != (b, B)):
         raise ValueError("inconsistent shapes")
     if max_prefix is None:

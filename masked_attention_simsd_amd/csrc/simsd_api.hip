@@ -72,7 +72,7 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   if (rc) return rc;
   if (max_prefix < 0) return SIMSD_ERR_SIZE;
   const uint32_t rule = flags & 3u;
-  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32))) return SIMSD_ERR_FLAGS;
+  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR))) return SIMSD_ERR_FLAGS;
   if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)))
@@ -113,6 +113,8 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   a.scale_log2 = sc * 1.4426950408889634f;
   a.data_rule = static_cast<int>(rule);
   a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
+  a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  a.xcd_remap = plan.xcd_remap;
   return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
 }
 

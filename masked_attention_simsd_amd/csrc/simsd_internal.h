@@ -83,11 +83,14 @@ struct AttnArgs {
   float scale_log2;   // softmax scale * log2(e)
   int data_rule;      // 0 causal, 1 bidirectional, 2 skip data rows
   int out_f32;
+  int xcd_remap;      // 1: workgroup ids remapped so a unit's splits share an XCD
+  int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
 };
 
 struct AttnPlan {
   int nwc, qb;        // compute waves and 16-row query blocks per wave
   int pipe;           // key-tile pipeline variant (keys per tile x ring stages)
+  int xcd_remap;
   int rows_per_wg;
   int row_slices;
   int chunk, nsplit;

@@ -110,6 +110,11 @@ __device__ __forceinline__ float sum_over_row_lanes(float x) {
 }
 
 // Wait until at most n vector-memory loads of this wave are outstanding.
+// Wait until tile t has landed when `ahead` younger tiles (DPW DMA instructions
+// each) may stay in flight: vmcnt(ahead * DPW), with ahead <= A.
+template <int DPW, int A>
+__device__ __forceinline__ void wait_tile(int ahead);
+
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0) only
 }
@@ -118,6 +123,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int DPW, int A>
+__device__ __forceinline__ void wait_tile(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A) wait_vmcnt<A * DPW>();
+    else wait_tile<DPW, A - 1>(ahead);
+  }
 }
 
 // XOR swizzles of the 16-byte chunks inside a key row of a staged tile. A K
@@ -165,6 +180,7 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   constexpr int MWG = NWC * QB * 16;  // query rows per workgroup
   static_assert(IPW >= 1 && (TK / RPI) % 4 == 0, "tile / wave mismatch");
   static_assert(NS >= 2 && (NS - 2) * DPW < 64, "pipeline depth");
+  static_assert(NS * STAGE_B <= 150 * 1024, "LDS ring");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE_B];
   __shared__ int tau_s[64];
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
 
   // ---- which (sequence, KV head, row slice, split) this workgroup owns ----
   const int wg = blockIdx.x;
-  const int logical = (wg & 7) * (a.total_grid >> 3) + (wg >> 3);
+  const int logical = a.xcd_remap ? (wg & 7) * (a.total_grid >> 3) + (wg >> 3) : wg;
   if (logical >= a.total_real) return;
   const int split = logical % a.nsplit;
   const int us = logical / a.nsplit;
@@ -196,9 +212,14 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   if (tid < 64) tau_s[tid] = tid < B ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
 
   // ---- tile schedule: prefix tiles of this chunk, then (split 0) the block ----
-  const uint32_t rsb = static_cast<uint32_t>(a.Hkv) * ROW_B;  // bytes between key rows
-  const char* kpre = reinterpret_cast<const char*>(a.k_pre + (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D);
-  const char* vpre = reinterpret_cast<const char*>(a.v_pre + (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D);
+  // prefix rows of (s, g): token-major [sum P][Hkv][d] or head-major [Hkv][sum P][d]
+  const uint32_t rsb = a.kv_head_major ? ROW_B : static_cast<uint32_t>(a.Hkv) * ROW_B;  // bytes between rows
+  const size_t pre0 = a.kv_head_major
+                          ? (static_cast<size_t>(g) * a.offsets[a.b] + a.offsets[s]) * D
+                          : (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D;
+  const char* kpre = reinterpret_cast<const char*>(a.k_pre + pre0);
+  const char* vpre = reinterpret_cast<const char*>(a.v_pre + pre0);
+  const uint32_t rsb_blk = static_cast<uint32_t>(a.Hkv) * ROW_B;  // block rows are [2B][Hkv][d]
   const char* kblk = reinterpret_cast<const char*>(a.k_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D);
   const char* vblk = reinterpret_cast<const char*>(a.v_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D);
   const int n_pre = (key_hi - key_lo + TK - 1) / TK;
@@ -206,9 +227,9 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   SIMSD_LDS uint8_t* const ring_l = (SIMSD_LDS uint8_t*)ring;
   const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_l));
 
-  // Per-lane byte offsets of the DMA of a full tile: instruction i of this wave
-  // fills LDS rows gi*RPI .. gi*RPI+RPI-1 (gi = 4i + wave); lane l supplies the
-  // chunk that the swizzle places in LDS slot l % CH of its row.
+  // Per-lane byte offsets of the DMA of a full prefix tile: instruction i of
+  // this wave fills LDS rows gi*RPI .. gi*RPI+RPI-1 (gi = 4i + wave); lane l
+  // supplies the chunk that the swizzle places in LDS slot l % CH of its row.
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
@@ -224,10 +245,11 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     const bool blk = t >= n_pre;
     const int r0 = blk ? (t - n_pre) * TK : key_lo + t * TK;
     const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
-    const char* kb = (blk ? kblk : kpre) + static_cast<size_t>(r0) * rsb;
-    const char* vb = (blk ? vblk : vpre) + static_cast<size_t>(r0) * rsb;
+    const uint32_t stride = blk ? rsb_blk : rsb;
+    const char* kb = (blk ? kblk : kpre) + static_cast<size_t>(r0) * stride;
+    const char* vb = (blk ? vblk : vpre) + static_cast<size_t>(r0) * stride;
     const uint32_t stage = ring_base + static_cast<uint32_t>((t % NS) * STAGE_B);
-    if (nvalid == TK) {
+    if (nvalid == TK && !blk) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
         const uint32_t lds = stage + static_cast<uint32_t>((i * 4 + wave) * 1024);
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
       for (int i = 0; i < IPW; ++i) {
         const int row = (i * 4 + wave) * RPI + lane / CH;
         const int p = lane % CH;
-        const uint32_t src = static_cast<uint32_t>(min(row, nvalid - 1)) * rsb;
+        const uint32_t src = static_cast<uint32_t>(min(row, nvalid - 1)) * stride;
         const uint32_t lds = stage + static_cast<uint32_t>((i * 4 + wave) * 1024);
         dma16(kb, src + 16u * static_cast<uint32_t>(p ^ swz_k<D>(row)), lds);
         dma16(vb, src + 16u * static_cast<uint32_t>(p ^ swz_v<D>(row)), lds + TENSOR_B);
@@ -303,17 +325,7 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
 
   for (int t = 0; t < ntiles; ++t) {
     // tile t must have landed; tiles t+1 .. t+NS-2 may still be in flight
-    const int ahead = min(NS - 2, ntiles - 1 - t);
-    if constexpr (NS >= 4) {
-      if (ahead >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * DPW>();
-      else if (ahead == 1) wait_vmcnt<DPW>();
-      else wait_vmcnt<0>();
-    } else if constexpr (NS == 3) {
-      if (ahead >= 1) wait_vmcnt<DPW>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_tile<DPW, NS - 2>(min(NS - 2, ntiles - 1 - t));
     block_barrier();  // every wave's share of tile t is in LDS; tile t-1 is consumed
     if (t + NS - 1 < ntiles) issue(t + NS - 1);
     if (!computes) continue;
@@ -548,6 +560,9 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
       case 1: return launch_variant<D, 4, 1, 64, 2>(a, stream);
       case 2: return launch_variant<D, 4, 1, 64, 3>(a, stream);
       case 3: return launch_variant<D, 4, 1, 32, 3>(a, stream);
+      case 4: return launch_variant<D, 4, 1, 32, 6>(a, stream);
+      case 5: return launch_variant<D, 4, 1, 32, 8>(a, stream);
+      case 6: return launch_variant<D, 4, 1, 64, 4>(a, stream);
       default: return launch_variant<D, 4, 1, 32, 4>(a, stream);
     }
   }
@@ -582,8 +597,10 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
   }
   p.rows_per_wg = p.nwc * p.qb * 16;
   // tuning override of the key-tile ring (keys per tile x stages) for d = 128,
-  // 4 x 16 rows: 0 = 32x4 (default), 1 = 64x2, 2 = 64x3, 3 = 32x3
+  // 4 x 16 rows: 0 = 32x4 (default), 1 = 64x2, 2 = 64x3, 3 = 32x3, 4 = 32x6,
+  // 5 = 32x8, 6 = 64x4
   p.pipe = env_int("SIMSD_ATTN_PIPE", 0);
+  p.xcd_remap = env_int("SIMSD_ATTN_XCD_REMAP", 1) != 0;  // tuning: keep a unit's splits on one XCD
   p.row_slices = (M + p.rows_per_wg - 1) / p.rows_per_wg;
   // About one workgroup per CU: each workgroup pays a pipeline fill and a
   // partial hand-off, so fewer, longer workgroups win once all CUs are busy.

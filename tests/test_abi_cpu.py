@@ -63,7 +63,7 @@ def test_attention_host_errors(lib):
     assert _attn(lib, Hq=6, Hkv=4) == 3
     assert _attn(lib, d=96) == 4
     assert _attn(lib, flags=3) == 5
-    assert _attn(lib, flags=8) == 5
+    assert _attn(lib, flags=16) == 5
     assert _attn(lib, scale=float("nan")) == 9
     assert _attn(lib, out=MISALIGNED) == 7
     assert _attn(lib, ws=None) == 6

@@ -19,7 +19,17 @@ TOL_BF16 = 2e-2
 TOL_F32 = 4e-3
 
 
+def head_major(x):
+    """The same inputs with the prefix cache stored [Hkv][sum P][d]."""
+    y = dict(x)
+    y["k_pre"] = x["k_pre"].transpose(0, 1).contiguous()
+    y["v_pre"] = x["v_pre"].transpose(0, 1).contiguous()
+    return y
+
+
 def run_gpu(x, flags=0, max_prefix=None, status=None, lse=True):
+    if flags & binding.SIMSD_KV_HEAD_MAJOR:
+        x = head_major(x)
     g = to_dev(x)
     b, twoB, Hq, _ = x["q_blk"].shape
     if max_prefix is None:
@@ -75,14 +85,17 @@ def test_shapes_match_oracle(shape, rule):
     compare(out, lse, ref, ref_lse, rule, TOL_F32, "fp32 out")
     out, lse = run_gpu(x, flags=rule)
     compare(out, lse, ref, ref_lse, rule, TOL_BF16, "bf16 out")
+    out, lse = run_gpu(x, flags=rule | binding.SIMSD_OUT_F32 | binding.SIMSD_KV_HEAD_MAJOR)
+    compare(out, lse, ref, ref_lse, rule, TOL_F32, "fp32 out, head-major cache")
 
 
+@pytest.mark.parametrize("layout", [0, binding.SIMSD_KV_HEAD_MAJOR], ids=["token_major", "head_major"])
 @pytest.mark.parametrize("cfg,seqs", [("tiny", None), ("b4", None), ("b8", None),
                                       ("b16", [0, 5]), ("ragged", None)])
-def test_workloads_match_oracle(cfg, seqs):
-    say(f"attention workload {cfg}")
+def test_workloads_match_oracle(cfg, seqs, layout):
+    say(f"attention workload {cfg} layout {layout}")
     x = inputs(cfg)
-    out, lse = run_gpu(x)
+    out, lse = run_gpu(x, flags=layout)
     if cfg == "ragged":
         lens = (x["prefix_offsets"][1:] - x["prefix_offsets"][:-1]).tolist()
         seqs = sorted({0, 1, 9, int(np.argmin(lens)), int(np.argmax(lens)), 33, 63})
