@@ -3,13 +3,17 @@
 One step = RoPE-copy -> verify attention -> acceptance over one batch of the
 headline workload (16 sequences, 32/8 heads, head_dim 128, prefix 4096, B=8,
 bf16 Q/K/V, vocab 32768), all launched on one stream with inputs resident in
-HBM. Several input sets are rotated so the 268 MB prefix KV of a step is not
-served from the 256 MB MALL.
+HBM. At least ceil(1 GB / prefix KV bytes) input sets are rotated so the
+prefix KV of a step is not served from the 256 MB MALL.
 
 Prints one JSON line: verified blocks/s (one block = one sequence's paired
 2B block through one attention layer plus acceptance), the attention kernel's
-HBM roofline figures (HIP events around every attention launch of the timed
-steps) and the CPU oracle's throughput on the host cores.
+HBM roofline figures (HIP events around back-to-back attention launches), each
+kernel's back-to-back time, the spread of per-step times, and the CPU
+oracle's throughput on the host cores (all cores, and one core).
+
+--workload selects another of the synthetic workloads (b4, b16, ragged) for
+the same measurement; the default is the headline one.
 """
 from __future__ import annotations
 
@@ -30,7 +34,11 @@ WORKLOAD = "b8"
 METRIC = "verified blocks/s + achieved HBM GB/s & MFMA % (B=8, 4K prefix, bf16)"
 ATTN_SOURCES = ("masked_attention_simsd_amd/csrc/verify_attention.hip",
                 "masked_attention_simsd_amd/csrc/simsd_internal.h")
-COUNTER_FILE = os.path.join(ROOT, "profiles", "verify_attention_b8_counters.txt")
+MALL_EVICT_BYTES = 1 << 30  # rotate at least this much prefix KV per pass over the sets
+
+
+def counter_file(workload):
+    return os.path.join(ROOT, "profiles", f"verify_attention_{workload}_counters.txt")
 
 
 def log(*a):
@@ -55,13 +63,15 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
+def counter_traffic(workload):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTER_FILE):
+    summary of `workload`, if it was taken on the current kernel source; else
+    None."""
+    path = counter_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTER_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -73,10 +83,24 @@ def counter_traffic():
         return None
 
 
-def cpu_baseline(x, threads):
-    """The oracle chain (RoPE-copy, attention, acceptance) on the whole batch,
-    repeated for about 10 s; returns (blocks/s, reps, seconds, result of the
-    first rep for the parity check)."""
+def subset(x, n):
+    """The inputs of the first n sequences (a bounded CPU sample)."""
+    import dataclasses
+
+    off = x["prefix_offsets"]
+    end = int(off[n])
+    y = {k: (v[:n] if v.dim() and v.shape[0] == x["workload"].b else v)
+         for k, v in x.items() if hasattr(v, "dim")}
+    y["prefix_offsets"] = off[:n + 1].clone()
+    y["k_pre"], y["v_pre"] = x["k_pre"][:end], x["v_pre"][:end]
+    y["workload"] = dataclasses.replace(x["workload"], b=n)
+    return y
+
+
+def cpu_baseline(x, threads, budget_s=10.0):
+    """The oracle chain (RoPE-copy, attention, acceptance) on the batch in x,
+    repeated for about budget_s; returns (blocks/s, reps, seconds, result of
+    the first rep for the parity check)."""
     import numpy as np
     import torch
 
@@ -101,7 +125,7 @@ def cpu_baseline(x, threads):
         if first is None:
             first = (out, acc)
         el = time.perf_counter() - t0
-        if el >= 10.0 or reps >= 20:
+        if el >= budget_s or reps >= 20:
             break
     return w.b * reps / el, reps, el, first
 
@@ -150,7 +174,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["b4", "b8", "b16", "ragged"])
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated across steps (default: enough to rotate 1 GB of prefix KV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration)")
@@ -177,11 +203,15 @@ def main():
         sys.exit(1)
     binding.load_library()  # fails loudly if libsimsd.so is missing
     dev = torch.device("cuda:0")
-    x = synth.make_inputs(WORKLOAD)
+    workload = args.workload
+    x = synth.make_inputs(workload)
     w = x["workload"]
     lens = x["prefix_lens"].tolist()
     max_prefix = max(lens)
-    log(f"workload {WORKLOAD}: {w.describe()}")
+    kv_bytes = 4 * w.d * w.Hkv * sum(lens)
+    if args.sets <= 0:
+        args.sets = min(256, max(2, -(-MALL_EVICT_BYTES // kv_bytes)))
+    log(f"workload {workload}: {w.describe()}; {args.sets} input sets")
 
     # The prefix cache is stored head-major ([Hkv][sum P][d], SIMSD_KV_HEAD_MAJOR):
     # each (sequence, KV head) split then streams one contiguous strip.
@@ -229,6 +259,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu_bps, reps, secs, (ref_out, ref_acc) = cpu_baseline(x, threads)
+        # one core, on the first sequences only (a bounded sample)
+        n1 = max(1, min(w.b, 2))
+        cpu1_bps, reps1, secs1, _ = cpu_baseline(subset(x, n1), 1, budget_s=5.0)
         err = float(np.abs(outs[0].to(torch.float64).cpu().numpy() - ref_out).max())
         L_ok = bool(np.array_equal(Ls[0].cpu().numpy(), ref_acc["accept_len"]))
         tok_ok = bool(((Cs[0].cpu().numpy() == ref_acc["correction"]) | ref_acc["boundary"].astype(bool)).all())
@@ -237,8 +270,10 @@ def main():
             print("parity check failed; not timing", file=sys.stderr)
             sys.exit(1)
         cpu = {"value": round(cpu_bps, 3), "unit": "blocks/s", "cores": threads, "kind": "oracle",
-               "sample": f"{reps} full batches of the {WORKLOAD} workload ({reps * b} blocks: "
-                         f"RoPE-copy + verify attention + acceptance, fp64 C oracle) in {secs:.1f} s"}
+               "sample": f"{reps} full batches of the {workload} workload ({reps * b} blocks: "
+                         f"RoPE-copy + verify attention + acceptance, fp64 C oracle) in {secs:.1f} s",
+               "single_core": {"value": round(cpu1_bps, 3), "unit": "blocks/s",
+                               "sample": f"{reps1} passes over the first {n1} sequences in {secs1:.1f} s"}}
 
     for i in range(args.warmup):
         step(i + 1)
@@ -265,10 +300,34 @@ def main():
     torch.cuda.synchronize()
     attn_avg_s = a0.elapsed_time(a1) / args.steps / 1e3
 
+    # each of the other kernels alone, back to back (RoPE-copy rotates the same
+    # buffers again each time: the same work)
+    def alone(fn, idx):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for i in range(args.steps):
+            if fn(*calls[i % len(calls)][idx]):
+                raise RuntimeError("libsimsd call failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    rope_us = alone(lib.simsd_rope_copy, 0)
+    acc_us = alone(lib.simsd_accept, 2)
+    # spread of single steps: an event pair around each step
+    pairs = [(ev(), ev()) for _ in range(min(args.steps, 200))]
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+    pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
+
     nbytes, flops = attn_bytes_flops(w, lens)
     achieved = nbytes / attn_avg_s / 1e9
     tflops = flops / attn_avg_s / 1e12
-    traffic = counter_traffic()
+    traffic = counter_traffic(workload)
     ai = flops / nbytes
     result = {
         "metric": METRIC,
@@ -283,7 +342,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD}: {w.describe()}", "global_batch": b,
+        "config": {"workload": f"{workload}: {w.describe()}", "global_batch": b,
                    "prefix": max_prefix, "block_B": B, "input_sets_rotated": args.sets,
                    "kv_cache_layout": "head-major [Hkv][sum P][d]",
                    "step": "rope_copy + verify_attention + accept"},
@@ -292,6 +351,9 @@ def main():
                      "traffic": traffic, "kernel": "verify_attn_kernel",
                      "avg_launch_us": round(attn_avg_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": nbytes},
+        "kernels_us": {"rope_copy": round(rope_us, 3), "verify_attention": round(attn_avg_s * 1e6, 3),
+                       "accept": round(acc_us, 3),
+                       "step_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)]},
         "attention_mfma": {"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
                            "ceiling_at_hbm_peak": round(min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS), 4),
                            "flops_per_launch": flops},

@@ -65,6 +65,9 @@ typedef enum {
 #define SIMSD_DEV_Q_ZERO 4        /* acceptance: q(x) == 0 met (accepted iff p(x) > 0) */
 #define SIMSD_DEV_BAD_TOKEN 8     /* acceptance: a draft id outside [0, V) (step rejected) */
 #define SIMSD_DEV_BAD_PREFIX 16   /* attention: P_s < 0 or P_s > max_prefix (P_s clamped into range) */
+#define SIMSD_DEV_SYNC_TIMEOUT 32 /* acceptance: a segment mass of this sequence was not seen within
+                                     the poll bound; the correction is unspecified and the workspace
+                                     must be zeroed again before reuse (not expected to occur) */
 
 /* simsd_rope_copy flags */
 #define SIMSD_ROPE_HALF 0u        /* rotate-half pairing (i, i + d/2) (default) */
@@ -184,13 +187,15 @@ size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, in
  * can differ from a sequential-sum reference only when u_{B+1} * Z lies within
  * rounding of a CDF step.
  *   status        optional int32 [b]: SIMSD_DEV_BAD_TAU (then L = 0,
- *                 correction -1), _ZERO_RESIDUAL, _Q_ZERO, _BAD_TOKEN
+ *                 correction -1), _ZERO_RESIDUAL, _Q_ZERO, _BAD_TOKEN,
+ *                 _SYNC_TIMEOUT
  *   workspace, ws_bytes  device scratch of at least simsd_accept_workspace()
- *                 bytes, 256-byte aligned: the first 256 KiB hold one counter
- *                 word per sequence and must be ZERO before the first call that
- *                 uses the buffer (every call leaves them zero again); the rest
- *                 holds per-segment residual masses. Calls sharing a workspace
- *                 must not run concurrently.
+ *                 bytes, 256-byte aligned, ALL ZERO before the first call that
+ *                 uses it (every call leaves it zero again): the first 256 KiB
+ *                 hold one arrival counter per sequence, the rest the
+ *                 per-segment residual masses the workgroups of a sequence
+ *                 publish to each other. Calls sharing a workspace must not
+ *                 run concurrently.
  * Errors: SIMSD_ERR_NULL, _SIZE (b<1 or b>65536, B not in 1..64, V<1 or
  * V>2^21), _ALIGN, _WORKSPACE, _LAUNCH.
  */

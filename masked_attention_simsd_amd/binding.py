@@ -23,7 +23,7 @@ SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY = 0, 1, 2
 SIMSD_DATA_CAUSAL, SIMSD_DATA_BIDIR, SIMSD_DATA_SKIP, SIMSD_OUT_F32 = 0, 1, 2, 4
 SIMSD_KV_HEAD_MAJOR = 8
 SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
-SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX = 8, 16
+SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
 
 EXPORTS = (
     "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_workspace",
@@ -144,7 +144,8 @@ def attention_workspace(device, nbytes: int):
 
 
 def accept_workspace(device, nbytes: int):
-    """As attention_workspace, for simsd_accept."""
+    """As attention_workspace, for simsd_accept (the whole buffer starts zero;
+    every call leaves it zero)."""
     return _cached_workspace("accept", device, nbytes)
 
 

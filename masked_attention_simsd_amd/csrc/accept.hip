@@ -8,21 +8,26 @@
 //
 // The step is latency bound, and one CU cannot keep enough misses in flight to
 // stream a 32K-151K vocabulary row quickly, so each sequence is spread over
-// ceil(V / 4096) workgroups of 256 threads (grid: segments x sequences).
+// ceil(V / (256 PER)) workgroups of 256 threads (grid: segments x sequences,
+// PER contiguous entries per thread).
 //   Phase 1 (wave 0 of every workgroup, one lane per temporal step t): tau and
 //   the draft ids are read together, tau is inverted in LDS, p[k][x] and
 //   q[k][x] are gathered at k = tau^-1(t), the IEEE fp32 ratio is compared
 //   with u_t, and one ballot gives the first rejected step L. Every workgroup
 //   of a sequence repeats this (a few gathers) so none waits for another.
-//   Phase 2 (only if L < B): each workgroup reads its 4096-entry segment of
-//   the rows p[k*], q[k*] (k* = tau^-1(L+1)), 16 contiguous entries per
-//   thread, and publishes the segment's fp64 residual mass max(0, p - q) with
-//   device-coherent stores. The last workgroup of the sequence (agent-scope
-//   counter) fetches all segment masses at once, forms Z in segment order,
-//   finds the segment holding T = u_{B+1} * Z and rescans it with a
+//   Phase 2 (only if L < B): each workgroup reads its segment of the rows
+//   p[k*], q[k*] (k* = tau^-1(L+1)), forms the segment's fp64 residual mass
+//   max(0, p - q) and publishes it with a ready bit, then bumps the sequence's
+//   agent-scope arrival counter without waiting for the publish to land. The
+//   last arrival polls the ready bits (every publish was issued before its
+//   counter bump, so each poll ends), clears the words for the next call,
+//   forms Z, finds the segment holding T = u_{B+1} * Z with a one-wave prefix
+//   scan over the segment masses, and rescans that segment with a
 //   workgroup-wide prefix sum for the first token whose running mass exceeds T.
 // Traffic: 2 V fp32 per rejecting sequence plus one segment re-read.
 #include "simsd_internal.h"
+
+#include <stdlib.h>
 
 namespace simsd {
 
@@ -30,17 +35,22 @@ namespace {
 
 constexpr int kAccThreads = 256;
 constexpr int kAccWaves = kAccThreads / kWave;
-constexpr int kPerThread = 16;                  // contiguous entries per thread
-constexpr int kSeg = kAccThreads * kPerThread;  // entries per segment / workgroup
+constexpr int kMinPer = 4;  // smallest entries-per-thread variant (sizes the workspace)
+constexpr int kMaxSegments = kMaxAcceptVocab / (kAccThreads * kMinPer);
+// A published segment mass carries this bit (masses are +0 or positive, so
+// the sign bit is free); a cleared word (0) means "not yet published".
+constexpr unsigned long long kReady = 1ull << 63;
+constexpr int kPollLimit = 1 << 16;  // bound on the polls of one mass word
 
-// Masses of entries y0 .. y0+15 of one row: the residual max(0, p - q) in
+// Masses of entries y0 .. y0+PER-1 of one row: the residual max(0, p - q) in
 // fp32, or p itself for the zero-residual fallback; entries at or past V are 0.
+template <int PER>
 __device__ __forceinline__ void load_masses(const float* prow, const float* qrow, int y0, int V,
-                                            bool vec, bool use_p, float w[kPerThread]) {
-  float pv[kPerThread], qv[kPerThread];
-  if (vec && y0 + kPerThread <= V) {
+                                            bool vec, bool use_p, float (&w)[PER]) {
+  float pv[PER], qv[PER];
+  if (vec && y0 + PER <= V) {
 #pragma unroll
-    for (int j = 0; j < kPerThread / 4; ++j) {
+    for (int j = 0; j < PER / 4; ++j) {
       const float4 a = *reinterpret_cast<const float4*>(prow + y0 + 4 * j);
       pv[4 * j] = a.x, pv[4 * j + 1] = a.y, pv[4 * j + 2] = a.z, pv[4 * j + 3] = a.w;
       const float4 b = use_p ? a : *reinterpret_cast<const float4*>(qrow + y0 + 4 * j);
@@ -48,22 +58,21 @@ __device__ __forceinline__ void load_masses(const float* prow, const float* qrow
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
+    for (int e = 0; e < PER; ++e) {
       const bool in = y0 + e < V;
       pv[e] = in ? prow[y0 + e] : 0.0f;
       qv[e] = (in && !use_p) ? qrow[y0 + e] : 0.0f;
     }
   }
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const float r = use_p ? pv[e] : pv[e] - qv[e];
     w[e] = r > 0.0f ? r : 0.0f;
   }
 }
 
-// Exclusive prefix sum (thread order) of one fp64 value per thread and the
-// workgroup total, which is computed as last exclusive prefix + last value so
-// that a rescan's running sums end exactly at the segment mass.
+// Exclusive prefix sum (thread order) of one fp64 value per thread, and the
+// workgroup total (last exclusive prefix + last value).
 __device__ double block_excl_scan(double v, double* total) {
   __shared__ double sh_wave[kAccWaves];
   __shared__ double sh_total;
@@ -88,17 +97,84 @@ __device__ double block_excl_scan(double v, double* total) {
   return excl;
 }
 
-__device__ __forceinline__ double thread_sum(const float w[kPerThread]) {
+// Sum of one fp64 value per thread over the workgroup (fixed order); the
+// result is valid in thread 0.
+__device__ double block_sum(double v) {
+  __shared__ double sh_wave[kAccWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  if (lane == 0) sh_wave[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (tid == 0)
+    for (int w = 0; w < kAccWaves; ++w) t += sh_wave[w];
+  __syncthreads();
+  return t;
+}
+
+template <int PER>
+__device__ __forceinline__ double thread_sum(const float (&w)[PER]) {
   double ls = 0.0;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) ls += static_cast<double>(w[e]);
+  for (int e = 0; e < PER; ++e) ls += static_cast<double>(w[e]);
   return ls;
 }
 
+// One wave over the segment masses m[0..nseg): Z = their sum (lanes own
+// contiguous runs of segments; run sums are combined by a lane scan). For
+// Z > 0 it picks the first segment j with m_j > 0 whose running sum passes
+// T = u * Z (rounding fallback: the last segment with positive mass) and
+// returns 1 with the running sum before it in *base; Z == 0 returns 0.
+__device__ int locate_segment(const double* m, int nseg, float u, int* seg_out, double* base_out,
+                              double* T_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (nseg + kWave - 1) / kWave;
+  const int j0 = min(lane * per, nseg), j1 = min(j0 + per, nseg);
+  double loc = 0.0;
+  for (int j = j0; j < j1; ++j) loc += m[j];
+  double incl = loc;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  const double Z = __shfl(incl, kWave - 1, kWave);
+  if (!(Z > 0.0)) return 0;
+  const double T = static_cast<double>(u) * Z;
+  int hit = -1, lastpos = -1;
+  double hit_base = 0.0, last_base = 0.0, run = excl;
+  for (int j = j0; j < j1; ++j) {
+    const double mj = m[j];
+    if (mj > 0.0) {
+      lastpos = j, last_base = run;
+      if (hit < 0 && run + mj > T) hit = j, hit_base = run;
+    }
+    run += mj;
+  }
+  const unsigned long long hits = __ballot(hit >= 0);
+  int src;
+  if (hits) {
+    src = __ffsll(static_cast<long long>(hits)) - 1;
+  } else {  // rounding left T at or past the total
+    const unsigned long long pos = __ballot(lastpos >= 0);
+    src = 63 - __clzll(static_cast<long long>(pos));
+    hit = lastpos, hit_base = last_base;
+  }
+  *seg_out = __shfl(hit, src, kWave);
+  *base_out = __shfl(hit_base, src, kWave);
+  *T_out = T;
+  return 1;
+}
+
+template <int PER>
 __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
+  constexpr int kSeg = kAccThreads * PER;  // entries per segment / workgroup
   __shared__ int inv_s[64];
   __shared__ int sh_L, sh_stat, sh_last, sh_pick, sh_seg;
-  __shared__ double sh_mass[kMaxAcceptVocab / kSeg];
+  __shared__ double sh_mass[kMaxSegments];
   __shared__ double sh_T, sh_base;
 
   const int seg = blockIdx.x, nseg = gridDim.x;
@@ -175,88 +251,90 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   const float* qrow = a.q + (static_cast<size_t>(s) * B + kstar) * V;
   const bool vec = (V % 4) == 0;
 
-  // ---- every workgroup: residual mass of its segment, published coherently ----
-  float w[kPerThread];
-  load_masses(prow, qrow, seg * kSeg + kPerThread * tid, V, vec, false, w);
-  double mine;
-  block_excl_scan(thread_sum(w), &mine);
-  double* segsum = a.seg_sum + static_cast<size_t>(s) * nseg;
-  if (tid == 0)
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(segsum + seg),
-                       static_cast<unsigned long long>(__double_as_longlong(mine)), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);  // the store is acknowledged before the counter moves
-  __syncthreads();
+  // ---- every workgroup: residual mass of its segment, published with the
+  // ready bit; the arrival counter moves without waiting for the publish ----
+  float w[PER];
+  load_masses<PER>(prow, qrow, seg * kSeg + PER * tid, V, vec, false, w);
+  const double mine = block_sum(thread_sum<PER>(w));
+  unsigned long long* words = reinterpret_cast<unsigned long long*>(a.seg_sum) +
+                              static_cast<size_t>(s) * nseg;
   if (tid == 0) {
+    __hip_atomic_store(words + seg, static_cast<unsigned long long>(__double_as_longlong(mine)) | kReady,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int prev = __hip_atomic_fetch_add(&a.counters[s], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_last = prev == nseg - 1;
   }
   __syncthreads();
   if (!sh_last) return;
 
-  // ---- last workgroup: all masses at once, threshold, segment, rescan ----
+  // ---- last workgroup: collect the masses, clear the words, locate ----
+  bool timed_out = false;
+  for (int j = tid; j < nseg; j += kAccThreads) {
+    if (j == seg) continue;  // own mass: thread 0 below
+    unsigned long long v;
+    int polls = 0;
+    do {
+      v = __hip_atomic_load(words + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v & kReady) break;
+      __builtin_amdgcn_s_sleep(1);
+    } while (++polls < kPollLimit);
+    timed_out |= !(v & kReady);
+    sh_mass[j] = __longlong_as_double(static_cast<long long>(v & ~kReady));
+    // cleared by the thread that read it: the clear lands after the publish
+    __hip_atomic_store(words + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) {
+    sh_mass[seg] = mine;
+    // own word: cleared by the thread that published it, after the publish
+    __hip_atomic_store(words + seg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (timed_out) atomicOr(&sh_stat, kDevSyncTimeout);
+  __syncthreads();
+
   bool use_p = false;
   for (int mode = 0; mode < 2; ++mode) {
     use_p = mode == 1;
-    if (!use_p) {
-      for (int j = tid; j < nseg; j += kAccThreads)
-        sh_mass[j] = __longlong_as_double(static_cast<long long>(__hip_atomic_load(
-            reinterpret_cast<unsigned long long*>(segsum + j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
-    } else {  // zero residual: the (rare) fallback draws from p; masses of p, all segments here
+    if (use_p) {  // zero residual: the (rare) fallback draws from p; masses of p, all segments here
       for (int j = 0; j < nseg; ++j) {
-        float wp[kPerThread];
-        load_masses(prow, qrow, j * kSeg + kPerThread * tid, V, vec, true, wp);
-        double m;
-        block_excl_scan(thread_sum(wp), &m);
+        float wp[PER];
+        load_masses<PER>(prow, qrow, j * kSeg + PER * tid, V, vec, true, wp);
+        const double m = block_sum(thread_sum<PER>(wp));
         if (tid == 0) sh_mass[j] = m;
       }
+      __syncthreads();
     }
-    __syncthreads();
-    if (tid == 0) {
-      double Z = 0.0;
-      for (int j = 0; j < nseg; ++j) Z += sh_mass[j];
-      if (Z > 0.0) {
-        const double T = static_cast<double>(u_corr) * Z;
-        double cum = 0.0, cum_last = 0.0;
-        int pick = -1, lastpos = -1;
-        for (int j = 0; j < nseg; ++j) {
-          const double m = sh_mass[j];
-          if (m > 0.0) lastpos = j, cum_last = cum;
-          if (cum + m > T) {
-            pick = j;
-            break;
-          }
-          cum += m;
+    if (wave == 0) {
+      int jseg;
+      double base, T;
+      const int found = locate_segment(sh_mass, nseg, u_corr, &jseg, &base, &T);
+      if (lane == 0) {
+        if (found) {
+          sh_seg = jseg;
+          sh_base = base;
+          sh_T = T;
+        } else {
+          sh_seg = -1;
+          if (mode == 0) sh_stat |= kDevZeroResidual;
         }
-        if (pick < 0) {  // rounding left T at or past the total
-          pick = lastpos;
-          cum = cum_last;
-        }
-        sh_seg = pick;
-        sh_base = cum;
-        sh_T = T;
-      } else {
-        sh_seg = -2;
-        if (mode == 0) sh_stat |= kDevZeroResidual;
       }
     }
     __syncthreads();
-    if (sh_seg != -2) break;
+    if (sh_seg >= 0) break;
   }
 
   if (tid == 0) sh_pick = 0x7fffffff;
   __syncthreads();
   const int j = sh_seg;  // < 0: no mass anywhere
   if (j >= 0) {
-    const int y0 = j * kSeg + kPerThread * tid;
-    if (j != seg || use_p) load_masses(prow, qrow, y0, V, vec, use_p, w);
+    const int y0 = j * kSeg + PER * tid;
+    if (j != seg || use_p) load_masses<PER>(prow, qrow, y0, V, vec, use_p, w);
     double total;
-    const double excl = block_excl_scan(thread_sum(w), &total);
+    const double excl = block_excl_scan(thread_sum<PER>(w), &total);
     const double T = sh_T, base = sh_base;
     int hit = -1, lastpos = -1;
     double run = 0.0;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
+    for (int e = 0; e < PER; ++e) {
       run += static_cast<double>(w[e]);
       if (w[e] > 0.0f) {
         lastpos = y0 + e;
@@ -284,13 +362,31 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   }
 }
 
+// Entries per thread (segment width / 256). SIMSD_ACCEPT_PER = 4, 8 or 16
+// overrides the default (read on every call).
+int accept_per(int b, int V) {
+  const char* e = getenv("SIMSD_ACCEPT_PER");
+  const int forced = e ? atoi(e) : 0;
+  if (forced == 4 || forced == 8 || forced == 16) return forced;
+  (void)b;
+  (void)V;
+  return 8;
+}
+
 }  // namespace
 
-int accept_segments(int V) { return (V + kSeg - 1) / kSeg; }
+int accept_segments(int V) { return (V + kAccThreads * kMinPer - 1) / (kAccThreads * kMinPer); }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(accept_segments(a.V)), static_cast<unsigned>(a.b));
-  hipLaunchKernelGGL(accept_kernel, grid, dim3(kAccThreads), 0, stream, a);
+  const int per = accept_per(a.b, a.V);
+  const int nseg = (a.V + kAccThreads * per - 1) / (kAccThreads * per);
+  dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(a.b));
+  if (per == 4)
+    hipLaunchKernelGGL(accept_kernel<4>, grid, dim3(kAccThreads), 0, stream, a);
+  else if (per == 8)
+    hipLaunchKernelGGL(accept_kernel<8>, grid, dim3(kAccThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(accept_kernel<16>, grid, dim3(kAccThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,43 +24,55 @@ namespace {
 constexpr int kRopeThreads = 256;
 constexpr int kMaxHalf = 64;  // d <= 128
 
-// One thread rotates 4 consecutive pairs of one head row.
-__device__ __forceinline__ void rotate4(uint16_t* row, int i0, int half, bool interleaved,
-                                        const double* cs, const double* sn) {
+// One thread rotates 4 consecutive pairs of one head row: rotate-half pairs
+// (i, i + half) come as two 8-byte pieces, interleaved pairs (2i, 2i+1) as one
+// 16-byte piece. The row is loaded first (before the angles are known) so the
+// memory latency overlaps the fp64 angle evaluation.
+struct Pairs4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Pairs4 load4(const uint16_t* row, int i0, int half, bool interleaved) {
+  Pairs4 v;
   if (!interleaved) {
-    // pairs (i, i + half) for i = i0 .. i0+3: two 8-byte loads
-    uint2 lo = *reinterpret_cast<const uint2*>(row + i0);
-    uint2 hi = *reinterpret_cast<const uint2*>(row + half + i0);
-    uint16_t a[4] = {static_cast<uint16_t>(lo.x), static_cast<uint16_t>(lo.x >> 16),
-                     static_cast<uint16_t>(lo.y), static_cast<uint16_t>(lo.y >> 16)};
-    uint16_t c[4] = {static_cast<uint16_t>(hi.x), static_cast<uint16_t>(hi.x >> 16),
-                     static_cast<uint16_t>(hi.y), static_cast<uint16_t>(hi.y >> 16)};
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + i0);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + half + i0);
+    v.w[0] = lo.x, v.w[1] = lo.y, v.w[2] = hi.x, v.w[3] = hi.y;
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(row + 2 * i0);
+    v.w[0] = a.x, v.w[1] = a.y, v.w[2] = a.z, v.w[3] = a.w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint16_t lo16(uint32_t w) { return static_cast<uint16_t>(w); }
+__device__ __forceinline__ uint16_t hi16(uint32_t w) { return static_cast<uint16_t>(w >> 16); }
+
+__device__ __forceinline__ void rotate_store4(uint16_t* row, int i0, int half, bool interleaved,
+                                              const Pairs4& v, const double* cs, const double* sn) {
+  if (!interleaved) {
+    // element j of the first half pairs with element j of the second half
+    const uint16_t a[4] = {lo16(v.w[0]), hi16(v.w[0]), lo16(v.w[1]), hi16(v.w[1])};
+    const uint16_t c[4] = {lo16(v.w[2]), hi16(v.w[2]), lo16(v.w[3]), hi16(v.w[3])};
     uint16_t ra[4], rc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      double xa = bf16_to_f32(a[j]), xb = bf16_to_f32(c[j]);
-      double co = cs[i0 + j], si = sn[i0 + j];
+      const double xa = bf16_to_f32(a[j]), xb = bf16_to_f32(c[j]);
+      const double co = cs[i0 + j], si = sn[i0 + j];
       ra[j] = f64_to_bf16(xa * co - xb * si);
       rc[j] = f64_to_bf16(xb * co + xa * si);
     }
-    lo.x = ra[0] | (static_cast<uint32_t>(ra[1]) << 16);
-    lo.y = ra[2] | (static_cast<uint32_t>(ra[3]) << 16);
-    hi.x = rc[0] | (static_cast<uint32_t>(rc[1]) << 16);
-    hi.y = rc[2] | (static_cast<uint32_t>(rc[3]) << 16);
-    *reinterpret_cast<uint2*>(row + i0) = lo;
-    *reinterpret_cast<uint2*>(row + half + i0) = hi;
+    *reinterpret_cast<uint2*>(row + i0) = make_uint2(ra[0] | (static_cast<uint32_t>(ra[1]) << 16),
+                                                     ra[2] | (static_cast<uint32_t>(ra[3]) << 16));
+    *reinterpret_cast<uint2*>(row + half + i0) = make_uint2(rc[0] | (static_cast<uint32_t>(rc[1]) << 16),
+                                                            rc[2] | (static_cast<uint32_t>(rc[3]) << 16));
   } else {
-    // pairs (2i, 2i+1) for i = i0 .. i0+3: one 16-byte load
-    uint4 v = *reinterpret_cast<const uint4*>(row + 2 * i0);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      double xa = bf16_to_f32(static_cast<uint16_t>(w[j]));
-      double xb = bf16_to_f32(static_cast<uint16_t>(w[j] >> 16));
-      double co = cs[i0 + j], si = sn[i0 + j];
-      uint16_t ra = f64_to_bf16(xa * co - xb * si);
-      uint16_t rb = f64_to_bf16(xb * co + xa * si);
-      w[j] = ra | (static_cast<uint32_t>(rb) << 16);
+      const double xa = bf16_to_f32(lo16(v.w[j])), xb = bf16_to_f32(hi16(v.w[j]));
+      const double co = cs[i0 + j], si = sn[i0 + j];
+      w[j] = f64_to_bf16(xa * co - xb * si) | (static_cast<uint32_t>(f64_to_bf16(xb * co + xa * si)) << 16);
     }
     *reinterpret_cast<uint4*>(row + 2 * i0) = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -71,53 +83,52 @@ __device__ __forceinline__ void rotate4(uint16_t* row, int i0, int half, bool in
 // does a single independent load / rotate / store.
 __global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a, int heads_per_wg) {
   __shared__ double cs_d[kMaxHalf], sn_d[kMaxHalf];  // angles of D_k
-  __shared__ double cs_t[kMaxHalf], sn_t[kMaxHalf];  // angles of D~_k (same unless no_copy)
+  __shared__ double cs_t[kMaxHalf], sn_t[kMaxHalf];  // angles of D~_k (only with no_copy)
   const int s = blockIdx.x / a.B;
   const int k = blockIdx.x % a.B;  // 0-based response position
   const int half = a.d / 2;
   const int tid = threadIdx.x;
-  const long pos_d = static_cast<long>(a.start_pos[s]) + k;
-  const long pos_t = a.no_copy ? pos_d + a.B : pos_d;
-  if (tid < half) {
-    const double inv_freq = pow(a.base, -2.0 * tid / a.d);
-    double ang = static_cast<double>(pos_d) * inv_freq;
-    sincos(ang, &sn_d[tid], &cs_d[tid]);
-    if (a.no_copy) {
-      ang = static_cast<double>(pos_t) * inv_freq;
-      sincos(ang, &sn_t[tid], &cs_t[tid]);
-    }
-  }
-  __syncthreads();
-  const double* cs = cs_d;
-  const double* sn = sn_d;
-  // items of this workgroup: (row slot, head in this chunk, group of 4 pairs)
+  // this thread's item: (row slot, head in this chunk, group of 4 pairs)
   const int groups = half / 4;
   const int heads = a.Hq + a.Hkv;
   const int h0 = blockIdx.y * heads_per_wg;
   const int nh = min(heads_per_wg, heads - h0);
   const int items = 2 * nh * groups;
-  for (int it = tid; it < items; it += kRopeThreads) {
-    const int grp = it % groups;
-    const int hh = h0 + (it / groups) % nh;
-    const int slot = it / (groups * nh);  // 0: D_k, 1: D~_k
-    const int r = k + slot * a.B;
-    uint16_t* row;
-    if (hh < a.Hq) {
-      row = a.q + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hq + hh) * a.d;
-    } else {
-      row = a.k + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hkv + (hh - a.Hq)) * a.d;
+  const bool active = tid < items;  // heads_per_wg is chosen so items <= blockDim
+  const int grp = tid % groups;
+  const int hh = h0 + (tid / groups) % nh;
+  const int slot = tid / (groups * nh);  // 0: D_k, 1: D~_k
+  const int r = k + slot * a.B;
+  uint16_t* row = hh < a.Hq ? a.q + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hq + hh) * a.d
+                            : a.k + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hkv + (hh - a.Hq)) * a.d;
+  Pairs4 v{};
+  if (active) v = load4(row, grp * 4, half, a.interleaved != 0);
+
+  const long pos_d = static_cast<long>(a.start_pos[s]) + k;
+  if (tid < half) {
+    const double inv_freq = pow(a.base, -2.0 * tid / a.d);
+    double ang = static_cast<double>(pos_d) * inv_freq;
+    sincos(ang, &sn_d[tid], &cs_d[tid]);
+    if (a.no_copy) {
+      ang = static_cast<double>(pos_d + a.B) * inv_freq;
+      sincos(ang, &sn_t[tid], &cs_t[tid]);
     }
+  }
+  __syncthreads();
+  if (active) {
     const bool use_t = slot && a.no_copy;
-    rotate4(row, grp * 4, half, a.interleaved != 0, use_t ? cs_t : cs, use_t ? sn_t : sn);
+    rotate_store4(row, grp * 4, half, a.interleaved != 0, v, use_t ? cs_t : cs_d, use_t ? sn_t : sn_d);
   }
 }
 
 }  // namespace
 
 hipError_t launch_rope_copy(const RopeArgs& a, hipStream_t stream) {
-  // one thread per (row slot, head, 4-pair group): 2 * groups items per head
+  // one thread per (row slot, head, 4-pair group): 2 * groups items per head,
+  // at most kRopeThreads items per workgroup
   const int groups = a.d / 8;
   const int heads_per_wg = std::max(1, kRopeThreads / (2 * groups));
+  static_assert(kRopeThreads % 32 == 0, "items per head divide the workgroup");
   const int heads = a.Hq + a.Hkv;
   dim3 grid(static_cast<unsigned>(a.b) * static_cast<unsigned>(a.B),
             static_cast<unsigned>((heads + heads_per_wg - 1) / heads_per_wg));

@@ -11,12 +11,13 @@ namespace simsd {
 constexpr int kWave = 64;
 constexpr int kMaxSeqCounters = 65536;  // counter words at the start of a workspace
 
-// Extra device status bit (kept beside the public ones in simsd.h).
+// Device status bits (the same values as SIMSD_DEV_* in simsd.h).
 constexpr int kDevBadTau = 1;
 constexpr int kDevZeroResidual = 2;
 constexpr int kDevQZero = 4;
 constexpr int kDevBadToken = 8;
 constexpr int kDevBadPrefix = 16;
+constexpr int kDevSyncTimeout = 32;
 
 // bf16 <-> fp32. bf16 is the upper half of an IEEE binary32.
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -108,7 +109,7 @@ struct AcceptArgs {
   int32_t* correction;
   int32_t* status;
   int32_t* counters;  // [b], zero between calls
-  double* seg_sum;    // [b][segments] residual mass per vocabulary segment
+  double* seg_sum;    // [b][segments] published residual mass words (ready bit), zero between calls
 };
 
 int accept_segments(int V);

@@ -40,12 +40,10 @@ def test_workloads_match_oracle(cfg):
     check(x["p"].numpy(), x["q"].numpy(), x["draft"].numpy(), x["tau"].numpy(), x["u"].numpy(), cfg)
 
 
-@pytest.mark.parametrize("V", [4, 7, 32768, 151936])
-def test_many_forced_rejections(V):
-    # Random distributions; every sequence rejects at a random step, so the
-    # residual draw runs for all of them.
-    rng = np.random.default_rng(V)
-    b, B = 256 if V < 100000 else 32, 8
+def rejecting_inputs(V, b, B=8, seed=None):
+    # Random distributions and uniformly drawn drafts: nearly every sequence
+    # rejects early, so the residual draw runs for almost all of them.
+    rng = np.random.default_rng(V if seed is None else seed)
     logits = rng.standard_normal((b, B, V)) * 2.0
     p = np.exp(logits - logits.max(-1, keepdims=True))
     p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
@@ -55,7 +53,36 @@ def test_many_forced_rejections(V):
     draft = rng.integers(0, V, (b, B)).astype(np.int32)
     tau = np.stack([rng.permutation(B) + 1 for _ in range(b)]).astype(np.int32)
     u = rng.random((b, B + 1)).astype(np.float32)
-    check(p, q, draft, tau, u, f"V={V}")
+    return p, q, draft, tau, u
+
+
+@pytest.mark.parametrize("V", [4, 7, 32768, 151936])
+def test_many_forced_rejections(V):
+    check(*rejecting_inputs(V, 256 if V < 100000 else 32), f"V={V}")
+
+
+@pytest.mark.parametrize("V,b", [(5001, 64), (32768, 64), (151936, 24)])
+def test_segment_widths_agree_and_leave_workspace_zero(V, b, monkeypatch):
+    # Every segment width (entries per thread 4 / 8 / 16) gives the oracle's
+    # lengths and, outside counted CDF-boundary cases, its tokens; each call
+    # leaves the whole workspace zero for the next one.
+    p, q, draft, tau, u = rejecting_inputs(V, b, seed=7)
+    ref = oracle.accept(p, q, draft, tau, u)
+    boundary = ref["boundary"].astype(bool)
+    dev = lambda a: torch.as_tensor(np.ascontiguousarray(a)).cuda()
+    args = [dev(a) for a in (p, q, draft, tau, u)]
+    ws = torch.zeros(binding.simsd_accept_workspace(b, 8, V), dtype=torch.uint8, device="cuda")
+    for per in ("4", "8", "16", "4"):
+        say(f"  V={V} b={b} entries per thread {per}")
+        monkeypatch.setenv("SIMSD_ACCEPT_PER", per)
+        status = torch.zeros(b, dtype=torch.int32, device="cuda")
+        L, corr = binding.simsd_accept(*args, status=status, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(L.cpu().numpy(), ref["accept_len"]), per
+        assert np.array_equal(status.cpu().numpy(), ref["status"]), per
+        diff = corr.cpu().numpy() != ref["correction"]
+        assert not (diff & ~boundary).any(), per
+        assert int(torch.count_nonzero(ws)) == 0, per
 
 
 def test_edge_cases():
