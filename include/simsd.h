@@ -132,7 +132,7 @@ int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, i
  *   out                  [b][2B][Hq][d], bf16 (or fp32 with SIMSD_OUT_F32)
  *   lse                  optional fp32 [b][2B][Hq]: natural-log sum of exp of
  *                        the allowed scores (NULL to skip)
- *   max_prefix           host int >= every P_s; it sizes the launch. A
+ *   max_prefix           host int >= every P_s, at most 2^30; it sizes the launch. A
  *                        sequence with P_s > max_prefix (or P_s < 0) is
  *                        computed with P_s clamped into [0, max_prefix] and
  *                        flagged SIMSD_DEV_BAD_PREFIX.

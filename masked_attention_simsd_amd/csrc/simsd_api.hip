@@ -53,7 +53,7 @@ int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, i
 }
 
 size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix) {
-  if (check_common(b, B, Hq, Hkv, d) || max_prefix < 0) return 0;
+  if (check_common(b, B, Hq, Hkv, d) || max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return 0;
   if (static_cast<long>(b) * Hkv * ((2L * B * (Hq / Hkv) + 127) / 128) > simsd::kAttnMaxUnits) return 0;
   // The data-row rule changes the row count and so the plan: size for both.
   const size_t all_rows = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 0).total_bytes;
@@ -70,7 +70,7 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   if (max_prefix > 0 && (!k_pre || !v_pre)) return SIMSD_ERR_NULL;
   int rc = check_common(b, B, Hq, Hkv, d);
   if (rc) return rc;
-  if (max_prefix < 0) return SIMSD_ERR_SIZE;
+  if (max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return SIMSD_ERR_SIZE;
   const uint32_t rule = flags & 3u;
   if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR))) return SIMSD_ERR_FLAGS;
   if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
@@ -115,6 +115,7 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
   a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
   a.xcd_remap = plan.xcd_remap;
+  a.rotate = plan.rotate;
   return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
 }
 

@@ -85,6 +85,7 @@ struct AttnArgs {
   int data_rule;      // 0 causal, 1 bidirectional, 2 skip data rows
   int out_f32;
   int xcd_remap;      // 1: workgroup ids remapped so a unit's splits share an XCD
+  int rotate;         // 1: each unit starts its prefix walk at its own tile
   int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
 };
 
@@ -92,6 +93,7 @@ struct AttnPlan {
   int nwc, qb;        // compute waves and 16-row query blocks per wave
   int pipe;           // key-tile pipeline variant (keys per tile x ring stages)
   int xcd_remap;
+  int rotate;
   int rows_per_wg;
   int row_slices;
   int chunk, nsplit;
@@ -117,7 +119,7 @@ int accept_segments(int V);
 constexpr int kMaxAcceptVocab = 1 << 21;  // vocabulary entries per row the acceptance kernel takes
 
 constexpr int kAttnTileKeys = 64;  // keys staged per tile
-constexpr int kAttnThreads = 256;
+constexpr int kMaxPrefix = 1 << 30; // largest max_prefix (key counts stay far from int overflow)
 constexpr int kAttnMaxUnits = kMaxSeqCounters;  // (sequence, KV head, row slice) units per call
 
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule);

@@ -161,28 +161,36 @@ __device__ __forceinline__ bool block_allowed(bool q_slot, int tau_q, int c, int
   return q_slot ? slot_row : data_row;
 }
 
-// D head dim; NWC compute waves x QB 16-row query blocks; TK keys per staged
+// D head dim; NW waves per workgroup (all issue the DMA), of which NWC x KS
+// compute: NWC row groups of QB 16-row query blocks, and KS waves per row
+// group that take disjoint slices of every key tile (KS = 2 puts two
+// independent waves on each SIMD, so one's MFMA work overlaps the other's
+// softmax; their states are merged through LDS at the end); TK keys per staged
 // tile; NS tiles in the LDS ring (NS - 1 in flight while one is consumed).
-template <int D, int NWC, int QB, int TKEYS, int NS, bool OUT_F32>
-__global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
+template <int D, int NW, int NWC, int QB, int TKEYS, int NS, int KS, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   constexpr int TK = TKEYS;         // keys per staged tile
   constexpr int KK = D / 32;          // MFMA k-steps of Q.K
   constexpr int DB = D / 16;          // 16-wide d blocks of P.V
   constexpr int CH = D / 8;           // 16-byte chunks per key row
   constexpr int ROW_B = D * 2;        // bytes per key row
   constexpr int RPI = 1024 / ROW_B;   // key rows per DMA wave instruction
-  constexpr int IPW = TK / RPI / 4;   // DMA instructions per wave per tensor per tile
+  constexpr int IPW = TK / RPI / NW;  // DMA instructions per wave per tensor per tile
   constexpr int DPW = 2 * IPW;        // ... for K and V together
   constexpr int TENSOR_B = TK * ROW_B;
   constexpr int STAGE_B = 2 * TENSOR_B;
-  constexpr int NSUB = TK / 32;       // 32-key PV steps per tile
-  constexpr int NKB = TK / 16;        // 16-key S^T blocks per tile
+  constexpr int TKW = TK / KS;        // keys of a tile per computing wave
+  constexpr int NSUB = TKW / 32;      // 32-key PV steps per tile and wave
+  constexpr int NKB = TKW / 16;       // 16-key S^T blocks per tile and wave
   constexpr int MWG = NWC * QB * 16;  // query rows per workgroup
-  static_assert(IPW >= 1 && (TK / RPI) % 4 == 0, "tile / wave mismatch");
+  static_assert(IPW >= 1 && (TK / RPI) % NW == 0 && NWC * KS <= NW, "tile / wave mismatch");
+  static_assert(TKW % 32 == 0 && (KS == 1 || KS == 2), "key slice per wave");
+  static_assert(KS == 1 || NWC * QB * (D / 16) * 64 * 16 <= NS * STAGE_B, "state exchange fits the ring");
   static_assert(NS >= 2 && (NS - 2) * DPW < 64, "pipeline depth");
   static_assert(NS * STAGE_B <= 150 * 1024, "LDS ring");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE_B];
+  __shared__ float xml[KS == 2 ? NWC * QB * 64 * 2 : 1];  // (m, l) handed between key slices
   __shared__ int tau_s[64];
   __shared__ int last_s;
 
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
 
   if (tid < 64) tau_s[tid] = tid < B ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
 
-  // ---- tile schedule: prefix tiles of this chunk, then (split 0) the block ----
+  // ---- tile schedule: (split 0) the block tiles, then the prefix tiles of this chunk ----
   // prefix rows of (s, g): token-major [sum P][Hkv][d] or head-major [Hkv][sum P][d]
   const uint32_t rsb = a.kv_head_major ? ROW_B : static_cast<uint32_t>(a.Hkv) * ROW_B;  // bytes between rows
   const size_t pre0 = a.kv_head_major
@@ -222,18 +230,29 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   const uint32_t rsb_blk = static_cast<uint32_t>(a.Hkv) * ROW_B;  // block rows are [2B][Hkv][d]
   const char* kblk = reinterpret_cast<const char*>(a.k_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D);
   const char* vblk = reinterpret_cast<const char*>(a.v_blk + (static_cast<size_t>(s) * twoB * a.Hkv + g) * D);
+  // split 0 takes the block tiles first: their rows live apart from the
+  // prefix strip, so their first-touch latency overlaps the prefix DMA
+  const int n_blk = split == 0 ? (twoB + TK - 1) / TK : 0;
   const int n_pre = (key_hi - key_lo + TK - 1) / TK;
-  const int ntiles = n_pre + (split == 0 ? (twoB + TK - 1) / TK : 0);
+  const int ntiles = n_blk + n_pre;
+  // Prefix tiles are visited from a per-unit starting tile (wrapping around),
+  // so that the many workgroups whose strips start at equally aligned
+  // addresses do not walk the same HBM channels in lockstep.
+  const int rot = (a.rotate && n_pre > 1) ? static_cast<int>((static_cast<unsigned>(us) * 2654435761u) >> 8) % n_pre : 0;
+  auto pre_tile = [&](int t) {  // prefix tile index of schedule slot t >= n_blk
+    const int j = t - n_blk + rot;
+    return j >= n_pre ? j - n_pre : j;
+  };
   SIMSD_LDS uint8_t* const ring_l = (SIMSD_LDS uint8_t*)ring;
   const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_l));
 
   // Per-lane byte offsets of the DMA of a full prefix tile: instruction i of
-  // this wave fills LDS rows gi*RPI .. gi*RPI+RPI-1 (gi = 4i + wave); lane l
+  // this wave fills LDS rows gi*RPI .. gi*RPI+RPI-1 (gi = NW i + wave); lane l
   // supplies the chunk that the swizzle places in LDS slot l % CH of its row.
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int row = (i * 4 + wave) * RPI + lane / CH;
+    const int row = (i * NW + wave) * RPI + lane / CH;
     const int p = lane % CH;
     koff[i] = static_cast<uint32_t>(row) * rsb + 16u * static_cast<uint32_t>(p ^ swz_k<D>(row));
     voff[i] = static_cast<uint32_t>(row) * rsb + 16u * static_cast<uint32_t>(p ^ swz_v<D>(row));
@@ -242,8 +261,8 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   // Issue the DMA of tile t into ring slot t % NS. In a partial tile, rows past
   // the valid end re-read the last valid row (in bounds; those keys are masked).
   auto issue = [&](int t) {
-    const bool blk = t >= n_pre;
-    const int r0 = blk ? (t - n_pre) * TK : key_lo + t * TK;
+    const bool blk = t < n_blk;
+    const int r0 = blk ? t * TK : key_lo + pre_tile(t) * TK;
     const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
     const uint32_t stride = blk ? rsb_blk : rsb;
     const char* kb = (blk ? kblk : kpre) + static_cast<size_t>(r0) * stride;
@@ -252,17 +271,17 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     if (nvalid == TK && !blk) {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
-        const uint32_t lds = stage + static_cast<uint32_t>((i * 4 + wave) * 1024);
+        const uint32_t lds = stage + static_cast<uint32_t>((i * NW + wave) * 1024);
         dma16(kb, koff[i], lds);
         dma16(vb, voff[i], lds + TENSOR_B);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
-        const int row = (i * 4 + wave) * RPI + lane / CH;
+        const int row = (i * NW + wave) * RPI + lane / CH;
         const int p = lane % CH;
         const uint32_t src = static_cast<uint32_t>(min(row, nvalid - 1)) * stride;
-        const uint32_t lds = stage + static_cast<uint32_t>((i * 4 + wave) * 1024);
+        const uint32_t lds = stage + static_cast<uint32_t>((i * NW + wave) * 1024);
         dma16(kb, src + 16u * static_cast<uint32_t>(p ^ swz_k<D>(row)), lds);
         dma16(vb, src + 16u * static_cast<uint32_t>(p ^ swz_v<D>(row)), lds + TENSOR_B);
       }
@@ -285,13 +304,17 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   }
 
   // ---- this lane's queries: one per 16-row block, row m of the unit ----
-  const bool computes = wave < NWC;
+  const bool computes = wave < NWC * KS;
+  const int rw = wave % NWC;   // row group
+  const int kh = wave / NWC;   // key slice of every tile (KS = 2)
+  const bool owner = computes && kh == 0;  // finishes the rows after the loop
+  const int kw0 = kh * TKW;                // first key of this wave's slice of a tile
   bf16x8 qreg[QB][KK];
   int tau_q[QB];
   bool slot_q[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int m = slice * MWG + (wave * QB + qb) * 16 + n16;
+    const int m = slice * MWG + (rw * QB + qb) * 16 + n16;
     const bool valid = computes && m < a.M;
     const int r = a.row0 + (valid ? m / a.G : 0);
     const int h = g * a.G + (valid ? m % a.G : 0);
@@ -305,6 +328,28 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     slot_q[qb] = r >= B;
     tau_q[qb] = tau_s[r >= B ? r - B : r];
   }
+  // Temporal mask of this lane's keys in the block tiles, evaluated once here
+  // (while the first tiles are in flight): bit (bt * NKB * 4 + kb * 4 + i) is
+  // key kw0 + 32(kb/2) + 8 a16 + 4(kb%2) + i of block tile bt, set if allowed.
+  static_assert(((128 + TK - 1) / TK) * NKB * 4 <= 64, "block mask bits");
+  uint64_t blk_bits[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    blk_bits[qb] = 0;
+    if (split == 0 && computes) {
+      const int nbt = (twoB + TK - 1) / TK;
+      for (int bt = 0; bt < nbt; ++bt)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = bt * TK + kw0 + 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
+            if (c < twoB && block_allowed(slot_q[qb], tau_q[qb], c, B, tau_s, a.data_rule))
+              blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
+          }
+    }
+  }
+
   // Make the compiler complete the Q loads here, not at their first use inside
   // the tile loop (a wait there would also drain the DMA ring every tile).
 #pragma unroll
@@ -330,18 +375,19 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     if (t + NS - 1 < ntiles) issue(t + NS - 1);
     if (!computes) continue;
 
-    const bool blk = t >= n_pre;
-    const int r0 = blk ? (t - n_pre) * TK : key_lo + t * TK;
+    const bool blk = t < n_blk;
+    const int r0 = blk ? t * TK : key_lo + pre_tile(t) * TK;
     const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
     SIMSD_LDS uint8_t* const kst_p = ring_l + (t % NS) * STAGE_B;
     SIMSD_LDS uint8_t* const vst_p = kst_p + TENSOR_B;
 
-    // S^T blocks: block kb covers keys 32(kb/2) + 8(m/4) + 4(kb%2) + m%4 for MFMA row m,
-    // so lane (a16, n16) ends up with keys 32ks + 8*a16 + 0..7 of query n16.
+    // S^T blocks: block kb covers keys 32(kb/2) + 8(m/4) + 4(kb%2) + m%4 for MFMA row m
+    // (relative to this wave's key slice kw0), so lane (a16, n16) ends up with keys
+    // kw0 + 32ks + 8*a16 + 0..7 of query n16.
     f32x4 sacc[QB][NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int row = 32 * (kb >> 1) + 8 * (n16 >> 2) + 4 * (kb & 1) + (n16 & 3);
+      const int row = kw0 + 32 * (kb >> 1) + 8 * (n16 >> 2) + 4 * (kb & 1) + (n16 & 3);
       const int sw = swz_k<D>(row);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -367,9 +413,9 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kl = 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
-            bool ok = kl < nvalid;
-            if (blk && ok) ok = block_allowed(slot_q[qb], tau_q[qb], r0 + kl, B, tau_s, a.data_rule);
+            const int kl = kw0 + 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
+            const bool ok = blk ? ((blk_bits[qb] >> (t * NKB * 4 + kb * 4 + i)) & 1ull) != 0
+                                : kl < nvalid;
             if (!ok) sacc[qb][kb][i] = -INFINITY;
           }
       }
@@ -418,7 +464,7 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
         i16x4 part[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int row = 32 * ks + 8 * a16 + 4 * hh + (n16 >> 2);
+          const int row = kw0 + 32 * ks + 8 * a16 + 4 * hh + (n16 >> 2);
           const int c = 2 * db + ((n16 & 3) >> 1);
           part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<SIMSD_LDS i16x4*>(
               vst_p + row * ROW_B + 16 * (c ^ swz_v<D>(row)) + 8 * (n16 & 1)));
@@ -433,6 +479,45 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb)
           oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.b, pop[qb][ks], oacc[qb][db], 0, 0, 0);
       }
+  }
+
+  if constexpr (KS == 2) {
+    // Fold the second key slice into the first: the slice-1 waves leave
+    // (m, lane-partial l, O) in LDS (the ring is free once every wave has
+    // left the loop), the slice-0 waves merge them with the log-sum-exp rule.
+    wait_lgkm0();
+    block_barrier();
+    float* xo = reinterpret_cast<float*>(ring);
+    if (computes && kh == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int slot = (rw * QB + qb) * 64 + lane;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<f32x4*>(xo + ((rw * QB + qb) * DB + db) * 256 + 4 * lane) = oacc[qb][db];
+        xml[2 * slot] = m_run[qb];
+        xml[2 * slot + 1] = l_run[qb];
+      }
+    }
+    wait_lgkm0();
+    block_barrier();
+    if (owner) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int slot = (rw * QB + qb) * 64 + lane;
+        const float m1 = xml[2 * slot], l1 = xml[2 * slot + 1];
+        const float m_new = fmaxf(m_run[qb], m1);
+        const float base = m_new == -INFINITY ? 0.0f : m_new;
+        const float wa = __builtin_amdgcn_exp2f((m_run[qb] - base) * c2);
+        const float wb = __builtin_amdgcn_exp2f((m1 - base) * c2);
+        l_run[qb] = l_run[qb] * wa + l1 * wb;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[qb][db] = oacc[qb][db] * wa +
+                         *reinterpret_cast<const f32x4*>(xo + ((rw * QB + qb) * DB + db) * 256 + 4 * lane) * wb;
+        m_run[qb] = m_new;
+      }
+    }
   }
 
   // ---- finish: full row sums, then either write or hand off to the merge ----
@@ -453,20 +538,20 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     constexpr int PART_O_B = NWC * QB * DB * 64 * 16;  // bytes of one split's O partial
     constexpr int PART_ML_B = MWG * 8;                  // bytes of one split's (m, l) pairs
     const size_t part = static_cast<size_t>(us) * a.nsplit + split;
-    if (computes) {
+    if (owner) {
       const auto ro = coherent_rsrc(reinterpret_cast<char*>(a.part_o) + part * PART_O_B, PART_O_B);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[qb][db]), ro,
-                                                 (((wave * QB + qb) * DB + db) * 64 + lane) * 16, 0, kCoherent);
+                                                 (((rw * QB + qb) * DB + db) * 64 + lane) * 16, 0, kCoherent);
       if (a16 == 0) {
         const auto rml = coherent_rsrc(reinterpret_cast<char*>(a.part_ml) + part * PART_ML_B, PART_ML_B);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           __builtin_amdgcn_raw_buffer_store_b64(
-              __builtin_bit_cast(u32x2, f32x2{m_sc[qb], l_tot[qb]}), rml, ((wave * QB + qb) * 16 + n16) * 8, 0,
+              __builtin_bit_cast(u32x2, f32x2{m_sc[qb], l_tot[qb]}), rml, ((rw * QB + qb) * 16 + n16) * 8, 0,
               kCoherent);
       }
     }
@@ -478,46 +563,70 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (!last_s) return;
-    if (computes) {
+    if (owner) {
+      // Online log-sum-exp merge of the ns partials in split order (fixed, so
+      // the result does not depend on which workgroup came last). The loads of
+      // MB partials are issued together: one memory round trip per MB splits.
+      constexpr int MB = QB == 1 ? 4 : 2;
       const size_t part0 = static_cast<size_t>(us) * a.nsplit;
       const auto ro = coherent_rsrc(reinterpret_cast<char*>(a.part_o) + part0 * PART_O_B, ns * PART_O_B);
       const auto rml = coherent_rsrc(reinterpret_cast<char*>(a.part_ml) + part0 * PART_ML_B, ns * PART_ML_B);
+      float m_acc[QB], l_acc[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int row = (wave * QB + qb) * 16 + n16;
-        float mmax = -INFINITY;
-        for (int k = 0; k < ns; ++k) {
-          const f32x2 ml = __builtin_bit_cast(
-              f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, k * PART_ML_B + row * 8, 0, kCoherent));
-          mmax = fmaxf(mmax, ml[0]);
-        }
-        const float m_use = mmax == -INFINITY ? 0.0f : mmax;
-        float lsum = 0.0f;
+        m_acc[qb] = -INFINITY;
+        l_acc[qb] = 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < ns; ++k) {
-          const f32x2 ml = __builtin_bit_cast(
-              f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, k * PART_ML_B + row * 8, 0, kCoherent));
-          const float w = __builtin_amdgcn_exp2f(ml[0] - m_use);
-          lsum += w * ml[1];
+      }
+      for (int k0 = 0; k0 < ns; k0 += MB) {
+        f32x2 ml[MB][QB];
+        f32x4 po[MB][QB][DB];
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            oacc[qb][db] += w * __builtin_bit_cast(
-                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               ro, k * PART_O_B + (((wave * QB + qb) * DB + db) * 64 + lane) * 16,
-                                               0, kCoherent));
+        for (int j = 0; j < MB; ++j) {
+          const int k = min(k0 + j, ns - 1);  // past the end: re-read the last one (ignored)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int row = (rw * QB + qb) * 16 + n16;
+            ml[j][qb] = __builtin_bit_cast(
+                f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, k * PART_ML_B + row * 8, 0, kCoherent));
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              po[j][qb][db] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             ro, k * PART_O_B + (((rw * QB + qb) * DB + db) * 64 + lane) * 16, 0, kCoherent));
+          }
         }
-        m_sc[qb] = mmax;
-        l_tot[qb] = lsum;
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          if (k0 + j >= ns) break;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float mk = ml[j][qb][0];
+            const float m_new = fmaxf(m_acc[qb], mk);
+            const float base = m_new == -INFINITY ? 0.0f : m_new;  // all empty so far: weights 0
+            const float wa = __builtin_amdgcn_exp2f(m_acc[qb] - base);
+            const float wb = __builtin_amdgcn_exp2f(mk - base);
+            l_acc[qb] = l_acc[qb] * wa + ml[j][qb][1] * wb;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[qb][db] = oacc[qb][db] * wa + po[j][qb][db] * wb;
+            m_acc[qb] = m_new;
+          }
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        m_sc[qb] = m_acc[qb];
+        l_tot[qb] = l_acc[qb];
       }
     }
     if (tid == 0) __hip_atomic_store(&a.counters[us], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  if (!computes) return;
+  if (!owner) return;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int m = slice * MWG + (wave * QB + qb) * 16 + n16;
+    const int m = slice * MWG + (rw * QB + qb) * 16 + n16;
     if (m >= a.M) continue;
     const int r = a.row0 + m / a.G;
     const int h = g * a.G + m % a.G;
@@ -540,13 +649,13 @@ __global__ __launch_bounds__(kAttnThreads) void verify_attn_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NWC, int QB, int TK, int NS>
+template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(a.total_grid)), block(kAttnThreads);
+  dim3 grid(static_cast<unsigned>(a.total_grid)), block(NW * 64);
   if (a.out_f32)
-    hipLaunchKernelGGL((verify_attn_kernel<D, NWC, QB, TK, NS, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((verify_attn_kernel<D, NWC, QB, TK, NS, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -554,7 +663,23 @@ template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2>(a, stream);
   if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2>(a, stream);
-  if (p.qb == 2) return launch_variant<D, 4, 2, 64, 2>(a, stream);
+  if (p.qb == 2 || p.nwc == 8) {
+    // 128 rows: 4 waves x 2 row blocks, or 8 waves x 1
+    if constexpr (D == 128) {
+      switch (p.pipe) {
+        case 1: return launch_variant<D, 4, 2, 32, 4>(a, stream);
+        case 2: return launch_variant<D, 4, 2, 64, 3>(a, stream);
+        case 3: return launch_variant<D, 8, 1, 32, 4, 8>(a, stream);
+        case 4: return launch_variant<D, 8, 1, 64, 2, 8>(a, stream);
+        case 5: return launch_variant<D, 8, 1, 32, 6, 8>(a, stream);
+        case 6: return launch_variant<D, 8, 1, 64, 3, 8>(a, stream);
+        case 7: return launch_variant<D, 4, 2, 64, 2, 8, 2>(a, stream);
+        case 8: return launch_variant<D, 4, 2, 64, 3, 8, 2>(a, stream);
+        default: return launch_variant<D, 4, 2, 64, 2>(a, stream);
+      }
+    }
+    return launch_variant<D, 4, 2, 64, 2>(a, stream);
+  }
   if constexpr (D == 128) {
     switch (p.pipe) {
       case 1: return launch_variant<D, 4, 1, 64, 2>(a, stream);
@@ -563,6 +688,9 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
       case 4: return launch_variant<D, 4, 1, 32, 6>(a, stream);
       case 5: return launch_variant<D, 4, 1, 32, 8>(a, stream);
       case 6: return launch_variant<D, 4, 1, 64, 4>(a, stream);
+      case 7: return launch_variant<D, 4, 1, 64, 2, 8, 2>(a, stream);
+      case 8: return launch_variant<D, 4, 1, 64, 3, 8, 2>(a, stream);
+      case 9: return launch_variant<D, 4, 1, 64, 4, 8, 2>(a, stream);
       default: return launch_variant<D, 4, 1, 32, 4>(a, stream);
     }
   }
@@ -578,9 +706,13 @@ int env_int(const char* name, int dflt) {
 }  // namespace
 
 // Launch plan: rows per workgroup from M = G * rows, then the number of
-// prefix splits so that about `target` workgroups cover the prefix, with
-// chunks no longer than `chunk_max` keys (keeps ragged batches balanced).
-// Tuning overrides: SIMSD_ATTN_TARGET_WG, SIMSD_ATTN_CHUNK_MAX.
+// prefix splits. Measured on MI355X: a workgroup streams fastest when it owns
+// one long contiguous run of keys, and every split adds a pipeline fill plus a
+// partial hand-off (fp32 O of all its rows written and read back), so the plan
+// splits only as far as needed to give each of the 256 CUs a workgroup:
+// units >= 256 run unsplit (a ragged batch then has all its workgroups
+// resident at once, two per CU), fewer units get ceil(256 / units) splits.
+// Tuning overrides: SIMSD_ATTN_TARGET_WG, SIMSD_ATTN_CHUNK_MAX, SIMSD_ATTN_PIPE.
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule) {
   AttnPlan p{};
   const int G = Hq / Hkv;
@@ -596,22 +728,25 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
     p.nwc = 4, p.qb = 2;
   }
   p.rows_per_wg = p.nwc * p.qb * 16;
-  // tuning override of the key-tile ring (keys per tile x stages) for d = 128,
-  // 4 x 16 rows: 0 = 32x4 (default), 1 = 64x2, 2 = 64x3, 3 = 32x3, 4 = 32x6,
-  // 5 = 32x8, 6 = 64x4
-  p.pipe = env_int("SIMSD_ATTN_PIPE", 0);
   p.xcd_remap = env_int("SIMSD_ATTN_XCD_REMAP", 1) != 0;  // tuning: keep a unit's splits on one XCD
+  p.rotate = env_int("SIMSD_ATTN_ROTATE", 1) != 0;        // tuning: per-unit starting prefix tile
   p.row_slices = (M + p.rows_per_wg - 1) / p.rows_per_wg;
-  // About one workgroup per CU: each workgroup pays a pipeline fill and a
-  // partial hand-off, so fewer, longer workgroups win once all CUs are busy.
   const int target = std::max(1, env_int("SIMSD_ATTN_TARGET_WG", 256));
-  const int chunk_max = std::max(TK, env_int("SIMSD_ATTN_CHUNK_MAX", 2048) / TK * TK);
+  const int chunk_max = std::max(TK, env_int("SIMSD_ATTN_CHUNK_MAX", 1 << 30) / TK * TK);
   const long units = static_cast<long>(b) * Hkv * p.row_slices;
   const int max_tiles = std::max(1, (max_prefix + TK - 1) / TK);
   int nsplit = static_cast<int>(std::min<long>(max_tiles, std::max<long>(1, (target + units - 1) / units)));
   int chunk = ((max_prefix + nsplit - 1) / nsplit + TK - 1) / TK * TK;
   chunk = std::max(TK, std::min(chunk, chunk_max));
   nsplit = std::max(1, (max_prefix + chunk - 1) / chunk);
+  // Key-tile ring (keys per tile x stages), for d = 128. 64 rows: 0 = 32x4,
+  // 1 = 64x2, 2 = 64x3, 3 = 32x3, 4 = 32x6, 5 = 32x8, 6 = 64x4. 128 rows:
+  // 0 = 4 waves x 2 row blocks 64x2, 1 = 4x2 32x4, 2 = 4x2 64x3, 3 = 8 waves
+  // x 1 32x4, 4 = 8x1 64x2, 5 = 8x1 32x6, 6 = 8x1 64x3. With one workgroup per
+  // CU the deeper 32x4 ring keeps more bytes in flight; with two per CU the
+  // other workgroup covers the latency and 64-key tiles halve the barriers.
+  const long wgs = units * nsplit;
+  p.pipe = env_int("SIMSD_ATTN_PIPE", (p.qb == 1 && wgs > 256) ? 1 : 0);
   p.chunk = chunk;
   p.nsplit = nsplit;
   const size_t us = static_cast<size_t>(units);

@@ -60,6 +60,7 @@ def test_attention_host_errors(lib):
     assert _attn(lib, B=65) == 2
     assert _attn(lib, B=0) == 2
     assert _attn(lib, maxp=-1) == 2
+    assert _attn(lib, maxp=(1 << 30) + 1) == 2
     assert _attn(lib, Hq=6, Hkv=4) == 3
     assert _attn(lib, d=96) == 4
     assert _attn(lib, flags=3) == 5
@@ -78,6 +79,8 @@ def test_workspace_sizes(lib):
     assert lib.simsd_verify_attention_workspace(1, 4, 8, 3, 128, 100) == 0
     assert lib.simsd_verify_attention_workspace(1, 4, 8, 2, 100, 100) == 0
     assert lib.simsd_verify_attention_workspace(1, 4, 8, 2, 128, -1) == 0
+    assert lib.simsd_verify_attention_workspace(1, 4, 8, 2, 128, (1 << 30) + 1) == 0
+    assert lib.simsd_verify_attention_workspace(1, 4, 8, 2, 128, 1 << 30) > 0
     for cfg in [(16, 8, 32, 8, 128, 4096), (8, 16, 32, 8, 128, 16384), (64, 8, 32, 8, 128, 8192),
                 (1, 4, 1, 1, 64, 32), (1, 64, 32, 8, 128, 100)]:
         n = lib.simsd_verify_attention_workspace(*cfg)

@@ -89,6 +89,20 @@ def test_shapes_match_oracle(shape, rule):
     compare(out, lse, ref, ref_lse, rule, TOL_F32, "fp32 out, head-major cache")
 
 
+@pytest.mark.parametrize("B", [8, 16], ids=["64_rows", "128_rows"])
+def test_every_kernel_variant_matches_oracle(B, monkeypatch):
+    # Each key-tile ring / wave layout the launcher can select (SIMSD_ATTN_PIPE)
+    # on a batch with several tiles per split, ragged tails and an empty prefix.
+    w = synth.custom(b=3, Hq=32, Hkv=8, d=128, B=B, prefix=(0, 2100))
+    x = synth.make_inputs(w, with_accept=False, seed=31 + B)
+    ref, ref_lse = run_oracle(x)
+    for pipe in range(10):
+        monkeypatch.setenv("SIMSD_ATTN_PIPE", str(pipe))
+        monkeypatch.setenv("SIMSD_ATTN_CHUNK_MAX", "512")
+        out, lse = run_gpu(x, flags=binding.SIMSD_OUT_F32 | binding.SIMSD_KV_HEAD_MAJOR)
+        compare(out, lse, ref, ref_lse, 0, TOL_F32, f"pipe {pipe}")
+
+
 @pytest.mark.parametrize("layout", [0, binding.SIMSD_KV_HEAD_MAJOR], ids=["token_major", "head_major"])
 @pytest.mark.parametrize("cfg,seqs", [("tiny", None), ("b4", None), ("b8", None),
                                       ("b16", [0, 5]), ("ragged", None)])
