@@ -3,7 +3,9 @@
 One step = RoPE-copy -> verify attention -> acceptance over one batch of the
 headline workload (16 sequences, 32/8 heads, head_dim 128, prefix 4096, B=8,
 bf16 Q/K/V, vocab 32768), all launched on one stream with inputs resident in
-HBM. At least ceil(1 GB / prefix KV bytes) input sets are rotated so the
+HBM. The form with RoPE-copy fused into the attention launch
+(simsd_verify_attention_rope, which also writes the rotated block keys) is
+timed beside it. At least ceil(1 GB / prefix KV bytes) input sets are rotated so the
 prefix KV of a step is not served from the 256 MB MALL.
 
 Prints one JSON line: verified blocks/s (one block = one sequence's paired
@@ -45,13 +47,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attn_bytes_flops(w, lens):
+def attn_bytes_flops(w, lens, fused=True):
     """Algorithmic bytes and flops of verify attention for prefix lengths `lens`:
     per sequence, bytes = K+V prefix (4 d Hkv P) + Q and O (bf16) + block K+V
-    (8 B d (Hq + Hkv)) + tau and offset (4B + 4); flops = 4 d Hq (2B P + B^2 +
-    B(B+1)/2) (mask slots see P + B keys, causal data rows P + tau(i))."""
+    (8 B d (Hq + Hkv)) + tau and offset (4B + 4), and with RoPE-copy fused the
+    rotated block keys written (4 B d Hkv) and the start position (4);
+    flops = 4 d Hq (2B P + B^2 + B(B+1)/2) (mask slots see P + B keys, causal
+    data rows P + tau(i))."""
     d, Hq, Hkv, B = w.d, w.Hq, w.Hkv, w.B
-    nbytes = sum(4 * d * Hkv * P + 8 * B * d * (Hq + Hkv) + 4 * B + 4 for P in lens)
+    extra = 4 * B * d * Hkv + 4 if fused else 0
+    nbytes = sum(4 * d * Hkv * P + 8 * B * d * (Hq + Hkv) + 4 * B + 4 + extra for P in lens)
     flops = sum(4 * d * Hq * (2 * B * P + B * B + B * (B + 1) // 2) for P in lens)
     return nbytes, flops
 
@@ -221,6 +226,7 @@ def main():
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.sets - 1)]
     b, B, Hq, Hkv, d = w.b, w.B, w.Hq, w.Hkv, w.d
     outs = [torch.empty_like(s["q_blk"]) for s in sets]
+    krots = [torch.empty_like(s["k_blk"]) for s in sets]
     Ls = [torch.empty(b, dtype=torch.int32, device=dev) for _ in sets]
     Cs = [torch.empty(b, dtype=torch.int32, device=dev) for _ in sets]
     ws = binding.attention_workspace(dev, binding.simsd_verify_attention_workspace(
@@ -242,12 +248,23 @@ def main():
                 ws.numel(), hs)
         acc = (P(s["p"]), P(s["q"]), P(s["draft"]), P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]),
                P(Cs[j]), None, P(ws_acc), ws_acc.numel(), hs)
-        calls.append((rope, attn, acc))
+        fused = (P(s["q_blk"]), P(s["k_blk"]), P(s["v_blk"]), P(s["k_pre"]), P(s["v_pre"]),
+                 P(s["prefix_offsets"]), P(s["tau"]), P(s["start_pos"]), ctypes.c_float(w.rope_base), 0,
+                 P(krots[j]), P(outs[j]), None, b, B, Hq, Hkv, d, max_prefix, ctypes.c_float(0.0),
+                 binding.SIMSD_KV_HEAD_MAJOR, None, P(ws), ws.numel(), hs)
+        calls.append((rope, attn, acc, fused))
 
     def step(i):
-        rope, attn, acc = calls[i % len(calls)]
+        rope, attn, acc, _ = calls[i % len(calls)]
         rc = lib.simsd_rope_copy(*rope)
         rc |= lib.simsd_verify_attention(*attn)
+        rc |= lib.simsd_accept(*acc)
+        if rc:
+            raise RuntimeError(f"libsimsd returned {rc}")
+
+    def step_fused(i):
+        _, _, acc, fused = calls[i % len(calls)]
+        rc = lib.simsd_verify_attention_rope(*fused)
         rc |= lib.simsd_accept(*acc)
         if rc:
             raise RuntimeError(f"libsimsd returned {rc}")
@@ -289,19 +306,11 @@ def main():
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
     blocks_per_s = b * args.steps / (total_ms / 1e3)
-    # timed region 2: the attention kernel alone, back to back on the same
-    # stream over the rotated input sets (its average launch duration)
-    a0, a1 = ev(), ev()
-    a0.record(stream)
-    for i in range(args.steps):
-        if lib.simsd_verify_attention(*calls[i % len(calls)][1]):
-            raise RuntimeError("simsd_verify_attention failed")
-    a1.record(stream)
-    torch.cuda.synchronize()
-    attn_avg_s = a0.elapsed_time(a1) / args.steps / 1e3
-
-    # each of the other kernels alone, back to back (RoPE-copy rotates the same
-    # buffers again each time: the same work)
+    # each kernel alone, back to back on the same stream over the rotated input
+    # sets (average launch duration); the attention kernel is the roofline
+    # kernel. The fused form runs first: RoPE-copy rotates q_blk / k_blk in
+    # place again on every call (the same work), which the fused form would
+    # otherwise read rotated several times over.
     def alone(fn, idx):
         e0, e1 = ev(), ev()
         e0.record(stream)
@@ -310,10 +319,19 @@ def main():
                 raise RuntimeError("libsimsd call failed")
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps * 1e3
+        return e0.elapsed_time(e1) / args.steps / 1e3
 
-    rope_us = alone(lib.simsd_rope_copy, 0)
-    acc_us = alone(lib.simsd_accept, 2)
+    fused_us = alone(lib.simsd_verify_attention_rope, 3) * 1e6
+    f0, f1 = ev(), ev()
+    f0.record(stream)
+    for i in range(args.steps):
+        step_fused(i)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fused_step_ms = f0.elapsed_time(f1) / args.steps
+    attn_avg_s = alone(lib.simsd_verify_attention, 1)
+    acc_us = alone(lib.simsd_accept, 2) * 1e6
+    rope_us = alone(lib.simsd_rope_copy, 0) * 1e6
     # spread of single steps: an event pair around each step
     pairs = [(ev(), ev()) for _ in range(min(args.steps, 200))]
     for i, (e0, e1) in enumerate(pairs):
@@ -324,7 +342,7 @@ def main():
     per_step = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
     pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
 
-    nbytes, flops = attn_bytes_flops(w, lens)
+    nbytes, flops = attn_bytes_flops(w, lens, fused=False)
     achieved = nbytes / attn_avg_s / 1e9
     tflops = flops / attn_avg_s / 1e12
     traffic = counter_traffic(workload)
@@ -353,7 +371,9 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes},
         "kernels_us": {"rope_copy": round(rope_us, 3), "verify_attention": round(attn_avg_s * 1e6, 3),
                        "accept": round(acc_us, 3),
-                       "step_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)]},
+                       "step_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
+                       "fused_rope": {"verify_attention_rope": round(fused_us, 3),
+                                      "step": round(fused_step_ms * 1e3, 3)}},
         "attention_mfma": {"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
                            "ceiling_at_hbm_peak": round(min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS), 4),
                            "flops_per_launch": flops},

@@ -14,9 +14,10 @@
  * tokens and a mask section D~ of B [MASK] slots (Methodologie 1), rotates the
  * block's queries and keys with the RoPE copy rule (Methodologie 3), runs one
  * attention pass under the temporal mask (Methodologie 2), and finally the
- * drafts are accepted or rejected along the draft's temporal order. The three
- * entry points below are the attention-layer and acceptance parts of that
- * step; projections, MLP and LM head are outside this library.
+ * drafts are accepted or rejected along the draft's temporal order. The entry
+ * points below are the attention-layer and acceptance parts of that step
+ * (RoPE-copy, attention, acceptance, and RoPE-copy fused into attention);
+ * projections, MLP and LM head are outside this library.
  *
  * Conventions common to every entry point
  *   - Every tensor argument is a DEVICE pointer owned by the caller. The
@@ -56,7 +57,8 @@ typedef enum {
   SIMSD_ERR_WORKSPACE = 6, /* workspace NULL, too small or not 256-byte aligned */
   SIMSD_ERR_ALIGN = 7,     /* a tensor pointer is not 16-byte aligned */
   SIMSD_ERR_LAUNCH = 8,    /* the HIP runtime refused a launch (see simsd_last_hip_error) */
-  SIMSD_ERR_SCALE = 9      /* rope_base <= 0 or a non-finite scale */
+  SIMSD_ERR_SCALE = 9,     /* rope_base <= 0 or a non-finite scale */
+  SIMSD_ERR_ALIAS = 10     /* an output overlaps an input it must not overlap */
 } simsd_status_t;
 
 /* Device status bits (int32 per sequence, OR-ed in). */
@@ -159,9 +161,39 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
                            int Hkv, int d, int max_prefix, float scale, uint32_t flags,
                            int32_t* status, void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes simsd_verify_attention needs for these sizes (0 on bad
- * sizes). */
+/* Workspace bytes simsd_verify_attention (and simsd_verify_attention_rope)
+ * needs for these sizes (0 on bad sizes). */
 size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix);
+
+/*
+ * simsd_verify_attention_rope -- the RoPE copy rule ([nl]/[fr] Methodologie
+ * 3: a mask slot D~_k takes the rotary position of its data token D_k) fused
+ * into the attention pass: the same result as simsd_rope_copy on q_blk and
+ * k_blk followed by simsd_verify_attention, in one launch, without modifying
+ * q_blk or k_blk. The query rows and the block key rows are rotated in
+ * registers with exactly the arithmetic of simsd_rope_copy (fp64 angles,
+ * cos/sin and rotation, one rounding to bf16), so out and lse are
+ * bit-identical to the two-call sequence.
+ *
+ *   q_blk, k_blk   bf16 [b][2B][Hq|Hkv][d] BEFORE RoPE (read only)
+ *   start_pos, rope_base, rope_flags  as for simsd_rope_copy
+ *   k_rot          optional bf16 [b][2B][Hkv][d] output: the rotated block
+ *                  keys (what simsd_rope_copy would leave in k_blk; the rows a
+ *                  KV-cache commit appends). Must not overlap k_blk. NULL to
+ *                  skip.
+ *   all other arguments as for simsd_verify_attention (the same workspace).
+ * The cos/sin table of the block positions lives in LDS:
+ * (NO_COPY ? 2B : B) * d <= 8192 (only d = 128 with SIMSD_ROPE_NO_COPY and
+ * B > 32 is refused, SIMSD_ERR_SIZE).
+ * Errors: those of simsd_verify_attention and simsd_rope_copy, and
+ * SIMSD_ERR_ALIAS (k_rot overlaps k_blk).
+ */
+int simsd_verify_attention_rope(const void* q_blk, const void* k_blk, const void* v_blk,
+                                const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                                const int32_t* tau, const int32_t* start_pos, float rope_base,
+                                uint32_t rope_flags, void* k_rot, void* out, float* lse, int b, int B,
+                                int Hq, int Hkv, int d, int max_prefix, float scale, uint32_t flags,
+                                int32_t* status, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * simsd_accept -- rejection-sampling acceptance along the draft's temporal

@@ -26,7 +26,8 @@ SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
 SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
 
 EXPORTS = (
-    "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_workspace",
+    "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_rope",
+    "simsd_verify_attention_workspace",
     "simsd_accept", "simsd_accept_workspace", "simsd_status_string", "simsd_last_hip_error",
 )
 
@@ -55,6 +56,9 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_rope_copy.restype = I
         lib.simsd_verify_attention.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, U, P, P, Z, P]
         lib.simsd_verify_attention.restype = I
+        lib.simsd_verify_attention_rope.argtypes = [P, P, P, P, P, P, P, P, F, U, P, P, P, I, I, I, I, I, I,
+                                                    F, U, P, P, Z, P]
+        lib.simsd_verify_attention_rope.restype = I
         lib.simsd_verify_attention_workspace.argtypes = [I, I, I, I, I, I]
         lib.simsd_verify_attention_workspace.restype = Z
         lib.simsd_accept.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, Z, P]
@@ -163,6 +167,31 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
     max_prefix: host int >= every prefix length; if None it is read back from
     prefix_offsets (a device-to-host copy, so not for timed loops).
     """
+    return _attention("simsd_verify_attention", q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets,
+                      tau, out, lse, max_prefix, scale, flags, status, workspace, stream, None)
+
+
+def simsd_verify_attention_rope(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, start_pos,
+                                rope_base: float = 10000.0, rope_flags: int = 0, k_rot=None, out=None,
+                                lse=None, max_prefix: int | None = None, scale: float = 0.0,
+                                flags: int = 0, status=None, workspace=None, stream=None):
+    """RoPE-copy fused into verify attention: q_blk / k_blk are the block rows
+    BEFORE RoPE and are not modified; k_rot (optional, [b][2B][Hkv][d] bf16,
+    not overlapping k_blk) receives the rotated block keys. Returns out."""
+    _need(start_pos, "start_pos", torch.int32, 1)
+    if start_pos.shape[0] != q_blk.shape[0]:
+        raise ValueError("start_pos must have b entries")
+    if k_rot is not None:
+        _need(k_rot, "k_rot", torch.bfloat16, 4)
+        if tuple(k_rot.shape) != tuple(k_blk.shape):
+            raise ValueError("k_rot shape must equal k_blk shape")
+    return _attention("simsd_verify_attention_rope", q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets,
+                      tau, out, lse, max_prefix, scale, flags, status, workspace, stream,
+                      (start_pos, float(rope_base), int(rope_flags), k_rot))
+
+
+def _attention(fn, q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, max_prefix,
+               scale, flags, status, workspace, stream, rope):
     for t, n in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk")):
         _need(t, n, torch.bfloat16, 4)
     for t, n in ((k_pre, "k_pre"), (v_pre, "v_pre")):
@@ -194,12 +223,17 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
     need = simsd_verify_attention_workspace(b, B, Hq, Hkv, d, max_prefix)
     if workspace is None:
         workspace = attention_workspace(q_blk.device, need)
-    rc = load_library().simsd_verify_attention(
-        _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre) if k_pre.numel() else None,
-        _ptr(v_pre) if v_pre.numel() else None, _ptr(prefix_offsets), _ptr(tau), _ptr(out),
-        _ptr(lse), b, B, Hq, Hkv, d, int(max_prefix), float(scale), flags, _ptr(status),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("simsd_verify_attention", rc)
+    head = (_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre) if k_pre.numel() else None,
+            _ptr(v_pre) if v_pre.numel() else None, _ptr(prefix_offsets), _ptr(tau))
+    tail = (_ptr(out), _ptr(lse), b, B, Hq, Hkv, d, int(max_prefix), float(scale), flags, _ptr(status),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    lib = load_library()
+    if rope is None:
+        rc = lib.simsd_verify_attention(*head, *tail)
+    else:
+        start_pos, base, rflags, k_rot = rope
+        rc = lib.simsd_verify_attention_rope(*head, _ptr(start_pos), base, rflags, _ptr(k_rot), *tail)
+    _check(fn, rc)
     return out
 
 

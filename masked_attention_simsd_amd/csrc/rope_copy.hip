@@ -12,7 +12,8 @@
 // The kernel is bound by latency and HBM traffic (one read + one write of the
 // block's Q and K); the head dimension of the grid gives every thread a single
 // rotation. fp64 is used for angles, cos/sin and the rotation, and each output
-// is rounded to bf16 once.
+// is rounded to bf16 once (the frequencies base^(-2i/d) are computed on the
+// host in fp64 and passed in the arguments).
 #include "simsd_internal.h"
 
 #include <algorithm>
@@ -56,12 +57,7 @@ __device__ __forceinline__ void rotate_store4(uint16_t* row, int i0, int half, b
     const uint16_t c[4] = {lo16(v.w[2]), hi16(v.w[2]), lo16(v.w[3]), hi16(v.w[3])};
     uint16_t ra[4], rc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const double xa = bf16_to_f32(a[j]), xb = bf16_to_f32(c[j]);
-      const double co = cs[i0 + j], si = sn[i0 + j];
-      ra[j] = f64_to_bf16(xa * co - xb * si);
-      rc[j] = f64_to_bf16(xb * co + xa * si);
-    }
+    for (int j = 0; j < 4; ++j) rope_rotate(a[j], c[j], cs[i0 + j], sn[i0 + j], &ra[j], &rc[j]);
     *reinterpret_cast<uint2*>(row + i0) = make_uint2(ra[0] | (static_cast<uint32_t>(ra[1]) << 16),
                                                      ra[2] | (static_cast<uint32_t>(ra[3]) << 16));
     *reinterpret_cast<uint2*>(row + half + i0) = make_uint2(rc[0] | (static_cast<uint32_t>(rc[1]) << 16),
@@ -70,9 +66,9 @@ __device__ __forceinline__ void rotate_store4(uint16_t* row, int i0, int half, b
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const double xa = bf16_to_f32(lo16(v.w[j])), xb = bf16_to_f32(hi16(v.w[j]));
-      const double co = cs[i0 + j], si = sn[i0 + j];
-      w[j] = f64_to_bf16(xa * co - xb * si) | (static_cast<uint32_t>(f64_to_bf16(xb * co + xa * si)) << 16);
+      uint16_t r0, r1;
+      rope_rotate(lo16(v.w[j]), hi16(v.w[j]), cs[i0 + j], sn[i0 + j], &r0, &r1);
+      w[j] = r0 | (static_cast<uint32_t>(r1) << 16);
     }
     *reinterpret_cast<uint4*>(row + 2 * i0) = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -106,7 +102,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a, int
 
   const long pos_d = static_cast<long>(a.start_pos[s]) + k;
   if (tid < half) {
-    const double inv_freq = pow(a.base, -2.0 * tid / a.d);
+    const double inv_freq = a.inv_freq[tid];
     double ang = static_cast<double>(pos_d) * inv_freq;
     sincos(ang, &sn_d[tid], &cs_d[tid]);
     if (a.no_copy) {

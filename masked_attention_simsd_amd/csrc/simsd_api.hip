@@ -22,6 +22,12 @@ int launch_status(hipError_t e) {
   return SIMSD_ERR_LAUNCH;
 }
 
+// RoPE frequencies base^(-2i/d), i < d/2, in fp64 (the same expression the
+// rotary embedding is defined by; computed once per call on the host).
+void fill_inv_freq(double* out, float base, int d) {
+  for (int i = 0; i < d / 2; ++i) out[i] = std::pow(static_cast<double>(base), -2.0 * i / d);
+}
+
 int check_common(int b, int B, int Hq, int Hkv, int d) {
   if (b < 1 || B < 1 || B > 64 || Hq < 1 || Hkv < 1) return SIMSD_ERR_SIZE;
   if (Hq % Hkv != 0) return SIMSD_ERR_HEADS;
@@ -29,43 +35,20 @@ int check_common(int b, int B, int Hq, int Hkv, int d) {
   return SIMSD_OK;
 }
 
-}  // namespace
+// Shared by simsd_verify_attention and simsd_verify_attention_rope (rope
+// points at the fused-RoPE arguments, or is NULL).
+struct RopeIn {
+  const int32_t* start_pos;
+  float base;
+  uint32_t flags;
+  void* k_rot;
+};
 
-extern "C" {
-
-int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, int B, int Hq,
-                    int Hkv, int d, float rope_base, uint32_t flags, void* stream) {
-  if (!q_blk || !k_blk || !start_pos) return SIMSD_ERR_NULL;
-  int rc = check_common(b, B, Hq, Hkv, d);
-  if (rc) return rc;
-  if (flags & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY)) return SIMSD_ERR_FLAGS;
-  if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return SIMSD_ERR_SCALE;
-  if (!aligned16(q_blk) || !aligned16(k_blk)) return SIMSD_ERR_ALIGN;
-  simsd::RopeArgs a{};
-  a.q = static_cast<uint16_t*>(q_blk);
-  a.k = static_cast<uint16_t*>(k_blk);
-  a.start_pos = start_pos;
-  a.b = b, a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.d = d;
-  a.base = static_cast<double>(rope_base);
-  a.interleaved = (flags & SIMSD_ROPE_INTERLEAVED) ? 1 : 0;
-  a.no_copy = (flags & SIMSD_ROPE_NO_COPY) ? 1 : 0;
-  return launch_status(simsd::launch_rope_copy(a, static_cast<hipStream_t>(stream)));
-}
-
-size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix) {
-  if (check_common(b, B, Hq, Hkv, d) || max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return 0;
-  if (static_cast<long>(b) * Hkv * ((2L * B * (Hq / Hkv) + 127) / 128) > simsd::kAttnMaxUnits) return 0;
-  // The data-row rule changes the row count and so the plan: size for both.
-  const size_t all_rows = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 0).total_bytes;
-  const size_t slots_only = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 2).total_bytes;
-  return all_rows > slots_only ? all_rows : slots_only;
-}
-
-int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_blk,
-                           const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
-                           const int32_t* tau, void* out, float* lse, int b, int B, int Hq,
-                           int Hkv, int d, int max_prefix, float scale, uint32_t flags,
-                           int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
+                          const void* v_pre, const int32_t* prefix_offsets, const int32_t* tau,
+                          void* out, float* lse, int b, int B, int Hq, int Hkv, int d, int max_prefix,
+                          float scale, uint32_t flags, int32_t* status, void* workspace,
+                          size_t ws_bytes, void* stream, const RopeIn* rope) {
   if (!q_blk || !k_blk || !v_blk || !prefix_offsets || !tau || !out) return SIMSD_ERR_NULL;
   if (max_prefix > 0 && (!k_pre || !v_pre)) return SIMSD_ERR_NULL;
   int rc = check_common(b, B, Hq, Hkv, d);
@@ -77,6 +60,20 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)))
     return SIMSD_ERR_ALIGN;
+  if (rope) {
+    if (!rope->start_pos) return SIMSD_ERR_NULL;
+    if (rope->flags & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY)) return SIMSD_ERR_FLAGS;
+    if (!(rope->base > 0.0f) || !std::isfinite(rope->base)) return SIMSD_ERR_SCALE;
+    // the cos/sin table lives in LDS beside the key ring
+    const long npos = (rope->flags & SIMSD_ROPE_NO_COPY) ? 2L * B : B;
+    if (npos * d * 8 > simsd::kMaxRopeTableBytes) return SIMSD_ERR_SIZE;
+    if (rope->k_rot) {
+      if (!aligned16(rope->k_rot)) return SIMSD_ERR_ALIGN;
+      const uintptr_t r0 = reinterpret_cast<uintptr_t>(rope->k_rot), k0 = reinterpret_cast<uintptr_t>(k_blk);
+      const uintptr_t n = static_cast<uintptr_t>(b) * 2 * B * Hkv * d * 2;
+      if (r0 < k0 + n && k0 < r0 + n) return SIMSD_ERR_ALIAS;
+    }
+  }
   const simsd::AttnPlan plan = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, static_cast<int>(rule));
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || ws_bytes < plan.total_bytes)
     return SIMSD_ERR_WORKSPACE;
@@ -103,6 +100,7 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   a.row_slices = plan.row_slices;
   a.chunk = plan.chunk;
   a.nsplit = plan.nsplit;
+  a.shift = plan.shift;
   a.max_prefix = max_prefix;
   if (static_cast<long>(b) * Hkv * plan.row_slices > simsd::kAttnMaxUnits) return SIMSD_ERR_SIZE;
   const long total = static_cast<long>(b) * Hkv * plan.row_slices * plan.nsplit;
@@ -116,7 +114,69 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
   a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
   a.xcd_remap = plan.xcd_remap;
   a.rotate = plan.rotate;
+  if (rope) {
+    a.rope = 1;
+    a.start_pos = rope->start_pos;
+    fill_inv_freq(a.rope_inv_freq, rope->base, d);
+    a.rope_interleaved = (rope->flags & SIMSD_ROPE_INTERLEAVED) ? 1 : 0;
+    a.rope_no_copy = (rope->flags & SIMSD_ROPE_NO_COPY) ? 1 : 0;
+    a.k_rot = static_cast<uint16_t*>(rope->k_rot);
+  }
   return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, int B, int Hq,
+                    int Hkv, int d, float rope_base, uint32_t flags, void* stream) {
+  if (!q_blk || !k_blk || !start_pos) return SIMSD_ERR_NULL;
+  int rc = check_common(b, B, Hq, Hkv, d);
+  if (rc) return rc;
+  if (flags & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY)) return SIMSD_ERR_FLAGS;
+  if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return SIMSD_ERR_SCALE;
+  if (!aligned16(q_blk) || !aligned16(k_blk)) return SIMSD_ERR_ALIGN;
+  simsd::RopeArgs a{};
+  a.q = static_cast<uint16_t*>(q_blk);
+  a.k = static_cast<uint16_t*>(k_blk);
+  a.start_pos = start_pos;
+  a.b = b, a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.d = d;
+  fill_inv_freq(a.inv_freq, rope_base, d);
+  a.interleaved = (flags & SIMSD_ROPE_INTERLEAVED) ? 1 : 0;
+  a.no_copy = (flags & SIMSD_ROPE_NO_COPY) ? 1 : 0;
+  return launch_status(simsd::launch_rope_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix) {
+  if (check_common(b, B, Hq, Hkv, d) || max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return 0;
+  if (static_cast<long>(b) * Hkv * ((2L * B * (Hq / Hkv) + 127) / 128) > simsd::kAttnMaxUnits) return 0;
+  // The data-row rule changes the row count and so the plan: size for both.
+  const size_t all_rows = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 0).total_bytes;
+  const size_t slots_only = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, 2).total_bytes;
+  return all_rows > slots_only ? all_rows : slots_only;
+}
+
+int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_blk,
+                           const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                           const int32_t* tau, void* out, float* lse, int b, int B, int Hq,
+                           int Hkv, int d, int max_prefix, float scale, uint32_t flags,
+                           int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+  return verify_attention_impl(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, b, B, Hq,
+                               Hkv, d, max_prefix, scale, flags, status, workspace, ws_bytes, stream,
+                               nullptr);
+}
+
+int simsd_verify_attention_rope(const void* q_blk, const void* k_blk, const void* v_blk,
+                                const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                                const int32_t* tau, const int32_t* start_pos, float rope_base,
+                                uint32_t rope_flags, void* k_rot, void* out, float* lse, int b, int B,
+                                int Hq, int Hkv, int d, int max_prefix, float scale, uint32_t flags,
+                                int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+  const RopeIn rope{start_pos, rope_base, rope_flags, k_rot};
+  return verify_attention_impl(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, b, B, Hq,
+                               Hkv, d, max_prefix, scale, flags, status, workspace, ws_bytes, stream,
+                               &rope);
 }
 
 size_t simsd_accept_workspace(int b, int B, int V) {
@@ -160,6 +220,7 @@ const char* simsd_status_string(int code) {
     case SIMSD_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case SIMSD_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case SIMSD_ERR_SCALE: return "rope_base or scale out of range";
+    case SIMSD_ERR_ALIAS: return "an output overlaps an input it must not overlap";
     default: return "unknown status";
   }
 }

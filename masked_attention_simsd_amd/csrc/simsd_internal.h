@@ -24,29 +24,42 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest even; NaN stays NaN (quiet).
+// Round to nearest even; NaN stays NaN (quiet). Branch-free (selects), so
+// it costs the same in every lane.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? qnan : rne);
 }
 
 // fp64 -> bf16 with a single rounding (nearest even). The double is first
 // narrowed to fp32 with round-to-odd, which keeps enough information for the
 // second, nearest-even narrowing to equal a direct one (fp32 carries 16 more
-// significand bits than bf16).
+// significand bits than bf16). Branch-free.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-  float f = static_cast<float>(x);  // nearest even
-  double back = static_cast<double>(f);
-  if (back != x && !__builtin_isnan(x) && !__builtin_isinf(f)) {
-    uint32_t u = __float_as_uint(f);
-    // step toward zero if the nearest-even result overshot in magnitude
-    if (__builtin_fabs(back) > __builtin_fabs(x)) u -= 1u;
-    u |= 1u;  // round to odd: inexact results get an odd last bit
-    f = __uint_as_float(u);
-  }
-  return f32_to_bf16(f);
+  const float f = static_cast<float>(x);  // nearest even
+  const double back = static_cast<double>(f);
+  const uint32_t u = __float_as_uint(f);
+  // inexact, finite result: step toward zero if nearest-even overshot in
+  // magnitude, then force the last bit to 1 (round to odd)
+  const bool adjust = back != x && !__builtin_isnan(x) && !__builtin_isinf(f);
+  const uint32_t down = __builtin_fabs(back) > __builtin_fabs(x) ? 1u : 0u;
+  const uint32_t odd = (u - down) | 1u;
+  return f32_to_bf16(__uint_as_float(adjust ? odd : u));
+}
+
+// RoPE arithmetic shared by the RoPE-copy kernel and the attention kernel's
+// fused prologue, so both round identically: the frequencies base^(-2i/d)
+// come from the host (fp64, once per call), the angle is pos * frequency,
+// cos/sin and the pair rotation are fp64 (explicit fma, no contraction left
+// to the compiler), and each output is rounded to bf16 once.
+constexpr int kMaxRopeFreqs = 64;  // d/2 for d <= 128
+__device__ __forceinline__ void rope_rotate(uint16_t xa, uint16_t xb, double co, double si,
+                                            uint16_t* ra, uint16_t* rb) {
+  const double a = bf16_to_f32(xa), b = bf16_to_f32(xb);
+  *ra = f64_to_bf16(__builtin_fma(a, co, -(b * si)));
+  *rb = f64_to_bf16(__builtin_fma(b, co, a * si));
 }
 
 struct RopeArgs {
@@ -54,8 +67,8 @@ struct RopeArgs {
   uint16_t* k;
   const int32_t* start_pos;
   int b, B, Hq, Hkv, d;
-  double base;
   int interleaved, no_copy;
+  double inv_freq[kMaxRopeFreqs];  // base^(-2i/d), i < d/2
 };
 
 struct AttnArgs {
@@ -77,6 +90,7 @@ struct AttnArgs {
   int M;              // query rows per (sequence, KV head) = nrows * G
   int row_slices;     // ceil(M / rows per workgroup)
   int chunk;          // prefix keys per split (multiple of the key tile)
+  int shift;          // split 0 runs chunk - shift keys, split k >= 1 starts at k * chunk - shift
   int nsplit;         // splits per (sequence, KV head, row slice)
   int max_prefix;
   int total_real;     // b * Hkv * row_slices * nsplit
@@ -87,6 +101,13 @@ struct AttnArgs {
   int xcd_remap;      // 1: workgroup ids remapped so a unit's splits share an XCD
   int rotate;         // 1: each unit starts its prefix walk at its own tile
   int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
+  // RoPE-copy fused into the prologue (rope != 0): query rows and block key
+  // rows are rotated on the fly; the rotated block keys go to k_rot if set
+  int rope;
+  const int32_t* start_pos;
+  int rope_interleaved, rope_no_copy;
+  uint16_t* k_rot;
+  double rope_inv_freq[kMaxRopeFreqs];  // base^(-2i/d), i < d/2
 };
 
 struct AttnPlan {
@@ -96,7 +117,7 @@ struct AttnPlan {
   int rotate;
   int rows_per_wg;
   int row_slices;
-  int chunk, nsplit;
+  int chunk, nsplit, shift;
   size_t counters_bytes, ml_bytes, o_bytes, total_bytes;
 };
 
@@ -120,6 +141,7 @@ constexpr int kMaxAcceptVocab = 1 << 21;  // vocabulary entries per row the acce
 
 constexpr int kAttnTileKeys = 64;  // keys staged per tile
 constexpr int kMaxPrefix = 1 << 30; // largest max_prefix (key counts stay far from int overflow)
+constexpr long kMaxRopeTableBytes = 64 * 1024;  // fused RoPE cos/sin table (LDS beside the key ring)
 constexpr int kAttnMaxUnits = kMaxSeqCounters;  // (sequence, KV head, row slice) units per call
 
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule);

@@ -161,13 +161,63 @@ __device__ __forceinline__ bool block_allowed(bool q_slot, int tau_q, int c, int
   return q_slot ? slot_row : data_row;
 }
 
+// RoPE-copy table row of block row r: data row D_{r+1} and (with the copy
+// rule) mask slot D~_{r-B+1} share position r resp. r - B; without the copy
+// rule the slot keeps its own row r (position start + r).
+__device__ __forceinline__ int rope_pos_row(int r, int B, int no_copy) {
+  return r < B ? r : (no_copy ? r : r - B);
+}
+
+// Rotate one query or key row held as this lane's KK chunks of 8 elements:
+// chunk kk holds elements 32 kk + 8 a16 + j. Rotate-half pairs element e with
+// e + D/2 (chunk kk + KK/2, same lane); interleaved pairs 2i with 2i + 1
+// (neighbours in one chunk). Table row `pr` holds (cos, sin) per frequency.
+template <int D, int KK>
+__device__ __forceinline__ void rope_rows(bf16x8 (&x)[KK], int pr, int a16, int interleaved,
+                                          const double* tab) {
+  const double* t = tab + static_cast<size_t>(pr) * D;  // D/2 (cos, sin) pairs
+  union U {
+    bf16x8 b;
+    uint16_t h[8];
+  };
+  if (!interleaved) {
+#pragma unroll
+    for (int kk = 0; kk < KK / 2; ++kk) {
+      U lo, hi;
+      lo.b = x[kk];
+      hi.b = x[kk + KK / 2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * kk + 8 * a16 + j;
+        rope_rotate(lo.h[j], hi.h[j], t[2 * i], t[2 * i + 1], &lo.h[j], &hi.h[j]);
+      }
+      x[kk] = lo.b;
+      x[kk + KK / 2] = hi.b;
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      U v;
+      v.b = x[kk];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int i = (32 * kk + 8 * a16 + j) / 2;
+        rope_rotate(v.h[j], v.h[j + 1], t[2 * i], t[2 * i + 1], &v.h[j], &v.h[j + 1]);
+      }
+      x[kk] = v.b;
+    }
+  }
+}
+
 // D head dim; NW waves per workgroup (all issue the DMA), of which NWC x KS
 // compute: NWC row groups of QB 16-row query blocks, and KS waves per row
 // group that take disjoint slices of every key tile (KS = 2 puts two
 // independent waves on each SIMD, so one's MFMA work overlaps the other's
 // softmax; their states are merged through LDS at the end); TK keys per staged
 // tile; NS tiles in the LDS ring (NS - 1 in flight while one is consumed).
-template <int D, int NW, int NWC, int QB, int TKEYS, int NS, int KS, bool OUT_F32>
+// ROPE: RoPE-copy fused into the prologue -- the query rows and the block key
+// rows are rotated on the fly from a per-workgroup cos/sin table (dynamic LDS).
+template <int D, int NW, int NWC, int QB, int TKEYS, int NS, int KS, bool ROPE, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   constexpr int TK = TKEYS;         // keys per staged tile
   constexpr int KK = D / 32;          // MFMA k-steps of Q.K
@@ -193,6 +243,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   __shared__ float xml[KS == 2 ? NWC * QB * 64 * 2 : 1];  // (m, l) handed between key slices
   __shared__ int tau_s[64];
   __shared__ int last_s;
+  extern __shared__ double rope_tab[];  // ROPE: [position][d/2] x (cos, sin)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps DMA math scalar
@@ -214,10 +265,15 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   P = P < 0 ? 0 : (P > a.max_prefix ? a.max_prefix : P);
   const int ns = P > 0 ? (P + a.chunk - 1) / a.chunk : 1;
   if (split >= ns) return;
-  const int key_lo = split * a.chunk;
-  const int key_hi = min(P, key_lo + a.chunk);
+  // split 0 also takes the block tiles, so its prefix run is `shift` keys
+  // shorter and every later boundary moves down by as much; the last split
+  // runs to the end of the prefix
+  const int key_lo = split == 0 ? 0 : split * a.chunk - a.shift;
+  const int key_hi = split == ns - 1 ? P : (split + 1) * a.chunk - a.shift;
 
-  if (tid < 64) tau_s[tid] = tid < B ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
+  // read before the first DMA is issued, so it can be a scalar load (the DMA
+  // asm clobbers memory as far as the compiler knows)
+  const long pos0 = ROPE ? static_cast<long>(a.start_pos[s]) : 0;
 
   // ---- tile schedule: (split 0) the block tiles, then the prefix tiles of this chunk ----
   // prefix rows of (s, g): token-major [sum P][Hkv][d] or head-major [Hkv][sum P][d]
@@ -292,8 +348,58 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   for (int t = 0; t < NS - 1; ++t)
     if (t < ntiles) issue(t);
 
+  // ---- tau and this lane's queries, requested right behind the first tiles
+  // (nothing before the ring fill waits on memory): one query per 16-row
+  // block, row m of the unit ----
+  const bool computes = wave < NWC * KS;
+  const int rw = wave % NWC;   // row group
+  const int kh = wave / NWC;   // key slice of every tile (KS = 2)
+  const bool owner = computes && kh == 0;  // finishes the rows after the loop
+  const int kw0 = kh * TKW;                // first key of this wave's slice of a tile
+  const int tau_ld = (tid < B) ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
+  // Lanes past the unit's M rows load (and later compute) a copy of its last
+  // row: their results are never stored, and unconditional loads keep the
+  // compiler from waiting on them (and so on the DMA ring) right here.
+  bf16x8 qreg[QB][KK];
+  int r_q[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int m = min(slice * MWG + (rw * QB + qb) * 16 + n16, a.M - 1);
+    const int r = a.row0 + m / a.G;
+    const int h = g * a.G + m % a.G;
+    const uint16_t* qrow = a.q_blk + ((static_cast<size_t>(s) * twoB + r) * a.Hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qreg[qb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * a16));
+    r_q[qb] = r;
+  }
+
+  if constexpr (ROPE) {
+    // cos/sin of every (block position, frequency) this workgroup needs,
+    // computed while the first tiles are in flight. Row p of the table is
+    // position start + p: the B data positions, then (without the copy rule)
+    // the B positions after them that the mask slots take instead. Entry e of
+    // the table has frequency e % (D/2) = lane % (D/2); each lane picks its
+    // frequency out of the kernel arguments with uniform (scalar) loads, so no
+    // vector load (whose wait would also drain the DMA ring) is needed here.
+    double inv_l = 0.0;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) inv_l = lane == k ? a.rope_inv_freq[k % (D / 2)] : inv_l;
+    const int npos = a.rope_no_copy ? twoB : B;
+    static_assert((NW * 64) % (D / 2) == 0, "table entries keep the lane's frequency");
+    for (int e = tid; e < npos * (D / 2); e += NW * 64) {
+      const int pi = e / (D / 2);
+      const double ang = static_cast<double>(pos0 + pi) * inv_l;
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      rope_tab[2 * e] = cs;
+      rope_tab[2 * e + 1] = sn;
+    }
+  }
+
+  if (tid < 64) tau_s[tid] = tau_ld;
   wait_lgkm0();
-  block_barrier();  // tau_s visible (the DMA above is not waited for here)
+  block_barrier();  // tau_s (and the RoPE table) visible
   if (a.status && split == 0 && slice == 0 && g == 0 && wave == 0) {
     int cnt = 0;
     if (lane < B)
@@ -303,30 +409,14 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
       atomicOr(&a.status[s], (bad_tau ? kDevBadTau : 0) | (bad_prefix ? kDevBadPrefix : 0));
   }
 
-  // ---- this lane's queries: one per 16-row block, row m of the unit ----
-  const bool computes = wave < NWC * KS;
-  const int rw = wave % NWC;   // row group
-  const int kh = wave / NWC;   // key slice of every tile (KS = 2)
-  const bool owner = computes && kh == 0;  // finishes the rows after the loop
-  const int kw0 = kh * TKW;                // first key of this wave's slice of a tile
-  bf16x8 qreg[QB][KK];
   int tau_q[QB];
   bool slot_q[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int m = slice * MWG + (rw * QB + qb) * 16 + n16;
-    const bool valid = computes && m < a.M;
-    const int r = a.row0 + (valid ? m / a.G : 0);
-    const int h = g * a.G + (valid ? m % a.G : 0);
-    const uint16_t* qrow = a.q_blk + ((static_cast<size_t>(s) * twoB + r) * a.Hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (valid) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * a16);
-      qreg[qb][kk] = as_bf16x8(v);
-    }
+    const int r = r_q[qb];
     slot_q[qb] = r >= B;
     tau_q[qb] = tau_s[r >= B ? r - B : r];
+    if constexpr (ROPE) rope_rows<D, KK>(qreg[qb], rope_pos_row(r, B, a.rope_no_copy), a16, a.rope_interleaved, rope_tab);
   }
   // Temporal mask of this lane's keys in the block tiles, evaluated once here
   // (while the first tiles are in flight): bit (bt * NKB * 4 + kb * 4 + i) is
@@ -368,13 +458,8 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t must have landed; tiles t+1 .. t+NS-2 may still be in flight
-    wait_tile<DPW, NS - 2>(min(NS - 2, ntiles - 1 - t));
-    block_barrier();  // every wave's share of tile t is in LDS; tile t-1 is consumed
-    if (t + NS - 1 < ntiles) issue(t + NS - 1);
-    if (!computes) continue;
-
+  // One tile's work for a computing wave: S^T, mask, online softmax, P.V.
+  auto compute_tile = [&](int t) {
     const bool blk = t < n_blk;
     const int r0 = blk ? t * TK : key_lo + pre_tile(t) * TK;
     const int nvalid = blk ? min(TK, twoB - r0) : min(TK, key_hi - r0);
@@ -479,6 +564,77 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb)
           oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.b, pop[qb][ks], oacc[qb][db], 0, 0, 0);
       }
+  };
+
+  // Pipeline step of tile t: wait until it has landed (tiles t+1 .. t+NS-2
+  // may still be in flight), one barrier (every wave's share of tile t is in
+  // LDS and tile t-1 is consumed), then refill the slot tile t-1 used.
+  auto advance = [&](int t) {
+    wait_tile<DPW, NS - 2>(min(NS - 2, ntiles - 1 - t));
+    block_barrier();
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
+  };
+
+  // Fused RoPE-copy: rotate the block key rows of a landed block tile in
+  // place in LDS, once per workgroup (every thread takes (row, pair-of-chunks)
+  // items), and write the rotated rows out for the cache if asked.
+  auto rotate_block_tile = [&](int t) {
+    const int r0 = t * TK;
+    SIMSD_LDS uint8_t* const kst_p = ring_l + (t % NS) * STAGE_B;
+    const bool write = a.k_rot != nullptr && split == 0 && slice == 0;
+    constexpr int HALF_CH = CH / 2;
+    const int per_row = a.rope_interleaved ? CH : HALF_CH;
+    for (int it = tid; it < TK * per_row; it += NW * 64) {
+      const int row = it / per_row, cc = it % per_row;
+      const int c = r0 + row;
+      if (c >= twoB) continue;
+      const int sw = swz_k<D>(row);
+      const double* tr = rope_tab + static_cast<size_t>(rope_pos_row(c, B, a.rope_no_copy)) * D;
+      union U {
+        u32x4 u;
+        uint16_t h[8];
+      };
+      SIMSD_LDS u32x4* pa = reinterpret_cast<SIMSD_LDS u32x4*>(kst_p + row * ROW_B + 16 * (cc ^ sw));
+      U x;
+      x.u = *pa;
+      if (a.rope_interleaved) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const int i = (8 * cc + j) / 2;
+          rope_rotate(x.h[j], x.h[j + 1], tr[2 * i], tr[2 * i + 1], &x.h[j], &x.h[j + 1]);
+        }
+        *pa = x.u;
+      } else {
+        SIMSD_LDS u32x4* pb = reinterpret_cast<SIMSD_LDS u32x4*>(kst_p + row * ROW_B + 16 * ((cc + HALF_CH) ^ sw));
+        U y;
+        y.u = *pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * cc + j;
+          rope_rotate(x.h[j], y.h[j], tr[2 * i], tr[2 * i + 1], &x.h[j], &y.h[j]);
+        }
+        *pa = x.u;
+        *pb = y.u;
+        if (write) {
+          uint16_t* dst = a.k_rot + ((static_cast<size_t>(s) * twoB + c) * a.Hkv + g) * D;
+          *reinterpret_cast<u32x4*>(dst + 8 * (cc + HALF_CH)) = y.u;
+        }
+      }
+      if (write) {
+        uint16_t* dst = a.k_rot + ((static_cast<size_t>(s) * twoB + c) * a.Hkv + g) * D;
+        *reinterpret_cast<u32x4*>(dst + 8 * cc) = x.u;
+      }
+    }
+    wait_lgkm0();
+    block_barrier();  // rotated rows visible to every wave
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    advance(t);
+    if constexpr (ROPE) {
+      if (t < n_blk) rotate_block_tile(t);
+    }
+    if (computes) compute_tile(t);
   }
 
   if constexpr (KS == 2) {
@@ -649,14 +805,35 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1>
+// Bytes of the fused RoPE table: (cos, sin) fp64 per (position, frequency).
+inline size_t rope_table_bytes(const AttnArgs& a) {
+  if (!a.rope) return 0;
+  const int npos = a.rope_no_copy ? 2 * a.B : a.B;
+  return static_cast<size_t>(npos) * (a.d / 2) * 2 * sizeof(double);
+}
+
+template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1, bool ROPE = false>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(a.total_grid)), block(NW * 64);
+  const size_t dyn = ROPE ? rope_table_bytes(a) : 0;
   if (a.out_f32)
-    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, ROPE, true>), grid, block, dyn, stream, a);
   else
-    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, ROPE, false>), grid, block, dyn, stream,
+                       a);
   return hipGetLastError();
+}
+
+// The fused-RoPE path instantiates only the variants the plan picks by default.
+template <int D>
+hipError_t launch_d_rope(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
+  if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2, 4, 1, true>(a, stream);
+  if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2, 4, 1, true>(a, stream);
+  if (p.qb == 2) return launch_variant<D, 4, 2, 64, 2, 4, 1, true>(a, stream);
+  if constexpr (D == 128) {
+    if (p.pipe != 1) return launch_variant<D, 4, 1, 32, 4, 4, 1, true>(a, stream);
+  }
+  return launch_variant<D, 4, 1, 64, 2, 4, 1, true>(a, stream);
 }
 
 template <int D>
@@ -749,6 +926,10 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
   p.pipe = env_int("SIMSD_ATTN_PIPE", (p.qb == 1 && wgs > 256) ? 1 : 0);
   p.chunk = chunk;
   p.nsplit = nsplit;
+  // prefix keys moved off split 0 to balance its block tiles (about one tile
+  // of prefix per block tile and 16-row query block); tuning: SIMSD_ATTN_SHIFT
+  const int blk_tiles = (2 * B + TK - 1) / TK;
+  p.shift = std::max(0, std::min(chunk / 2, env_int("SIMSD_ATTN_SHIFT", TK * blk_tiles * p.qb)));
   const size_t us = static_cast<size_t>(units);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   // The counter words sit in a region of fixed size at the start of every
@@ -762,6 +943,7 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
 }
 
 hipError_t launch_verify_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
+  if (a.rope) return a.d == 64 ? launch_d_rope<64>(a, p, stream) : launch_d_rope<128>(a, p, stream);
   if (a.d == 64) return launch_d<64>(a, p, stream);
   return launch_d<128>(a, p, stream);
 }

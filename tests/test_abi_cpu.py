@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         assert lib.simsd_status_string(code)
     assert lib.simsd_status_string(0) == b"ok"
 
@@ -72,6 +72,34 @@ def test_attention_host_errors(lib):
     need = lib.simsd_verify_attention_workspace(2, 4, 8, 2, 128, 100)
     assert need > 0
     assert _attn(lib, wsb=need - 1) == 6
+
+
+def _attn_rope(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, off=FAKE, tau=FAKE, sp=FAKE, base=10000.0,
+             rflags=0, krot=None, out=FAKE, lse=None, b=2, B=4, Hq=8, Hkv=2, d=128, maxp=100,
+             scale=0.0, flags=0, status=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.simsd_verify_attention_rope(a["q"], a["k"], a["v"], a["kp"], a["vp"], a["off"], a["tau"],
+                                           a["sp"], a["base"], a["rflags"], a["krot"], a["out"], a["lse"],
+                                           a["b"], a["B"], a["Hq"], a["Hkv"], a["d"], a["maxp"], a["scale"],
+                                           a["flags"], a["status"], a["ws"], a["wsb"], None)
+
+
+def test_fused_rope_attention_host_errors(lib):
+    assert _attn_rope(lib, sp=None) == 1
+    assert _attn_rope(lib, q=None) == 1
+    assert _attn_rope(lib, rflags=4) == 5
+    assert _attn_rope(lib, flags=3) == 5
+    assert _attn_rope(lib, base=0.0) == 9
+    assert _attn_rope(lib, base=float("nan")) == 9
+    assert _attn_rope(lib, krot=MISALIGNED) == 7
+    # the cos/sin table: (NO_COPY ? 2B : B) * d <= 8192
+    assert _attn_rope(lib, B=33, rflags=2) == 2
+    assert _attn_rope(lib, B=64, rflags=2, d=64, Hq=8, Hkv=2) != 2
+    # k_rot overlapping k_blk: [b][2B][Hkv][d] bf16 = 2*8*2*128*2 bytes
+    assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 4096)) == 10
+    assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 8192)) != 10
+    assert lib.simsd_status_string(10)
 
 
 def test_workspace_sizes(lib):
