@@ -161,17 +161,17 @@ def summarize_rocprof(path: str):
     for f in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
         print(f"# kernel stats: {os.path.relpath(f, path)}")
         for r in csv.DictReader(open(f)):
-            print(f"{r['Name'][:90]:90s} calls {int(r['Calls']):6d}  avg_us {float(r['AverageNs']) / 1e3:10.3f}"
+            print(f"{r['Name'][:112]:112s} calls {int(r['Calls']):6d}  avg_us {float(r['AverageNs']) / 1e3:10.3f}"
                   f"  min_us {float(r['MinNs']) / 1e3:10.3f}  max_us {float(r['MaxNs']) / 1e3:10.3f}"
                   f"  pct {float(r['Percentage']):6.2f}")
     for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
         print(f"# counters: {os.path.relpath(f, path)}")
         acc = {}
         for r in csv.DictReader(open(f)):
-            key = (r["Kernel_Name"][:90], r["Counter_Name"])
+            key = (r["Kernel_Name"][:112], r["Counter_Name"])
             acc.setdefault(key, []).append(float(r["Counter_Value"]))
         for (k, c), v in sorted(acc.items()):
-            print(f"{k:90s} {c:12s} dispatches {len(v):5d}  mean_per_dispatch {statistics.fmean(v):16.1f}")
+            print(f"{k:112s} {c:12s} dispatches {len(v):5d}  mean_per_dispatch {statistics.fmean(v):16.1f}")
 
 
 def main():

@@ -926,10 +926,9 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
   p.pipe = env_int("SIMSD_ATTN_PIPE", (p.qb == 1 && wgs > 256) ? 1 : 0);
   p.chunk = chunk;
   p.nsplit = nsplit;
-  // prefix keys moved off split 0 to balance its block tiles (about one tile
-  // of prefix per block tile and 16-row query block); tuning: SIMSD_ATTN_SHIFT
-  const int blk_tiles = (2 * B + TK - 1) / TK;
-  p.shift = std::max(0, std::min(chunk / 2, env_int("SIMSD_ATTN_SHIFT", TK * blk_tiles * p.qb)));
+  // tuning: prefix keys moved off split 0, which also takes the block tiles
+  // (SIMSD_ATTN_SHIFT; measured neutral on MI355X, so 0 by default)
+  p.shift = std::max(0, std::min(chunk / 2, env_int("SIMSD_ATTN_SHIFT", 0)));
   const size_t us = static_cast<size_t>(units);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   // The counter words sit in a region of fixed size at the start of every
