@@ -95,7 +95,8 @@ def make_inputs(w: Workload | str, seed: int | None = None, with_accept: bool = 
     prefix_lens [b] int64, prefix_offsets [b+1] int32, start_pos [b] int32,
     k_pre / v_pre [sum P][Hkv][d] bf16, q_blk [b][2B][Hq][d] bf16,
     k_blk / v_blk [b][2B][Hkv][d] bf16, tau [b][B] int32 (labels 1..B),
-    p / q [b][B][V] fp32, draft [b][B] int32, u [b][B+1] fp32.
+    p / q [b][B][V] fp32 (softmax of target_logits / draft_logits [b][B][V]
+    fp32), draft [b][B] int32, u [b][B+1] fp32.
     """
     if isinstance(w, str):
         w = CONFIGS[w]
@@ -131,13 +132,20 @@ def make_inputs(w: Workload | str, seed: int | None = None, with_accept: bool = 
         V = w.V
         p = torch.empty((b, B, V), dtype=torch.float32)
         q = torch.empty((b, B, V), dtype=torch.float32)
+        zt = torch.empty((b, B, V), dtype=torch.float32)
+        zd = torch.empty((b, B, V), dtype=torch.float32)
         for s in range(b):  # per sequence to bound fp64 temporaries
             tgt = torch.randn((B, V), generator=g, dtype=torch.float64) * w.logit_std
             drf = tgt + torch.randn((B, V), generator=g, dtype=torch.float64) * w.noise_std
-            p[s] = torch.softmax(tgt, dim=-1).to(torch.float32)
-            q[s] = torch.softmax(drf, dim=-1).to(torch.float32)
+            # the logits are stored in fp32; the probabilities are their fp64
+            # softmax rounded to fp32
+            zt[s] = tgt.to(torch.float32)
+            zd[s] = drf.to(torch.float32)
+            p[s] = torch.softmax(zt[s].to(torch.float64), dim=-1).to(torch.float32)
+            q[s] = torch.softmax(zd[s].to(torch.float64), dim=-1).to(torch.float32)
         draft = torch.multinomial(q.reshape(b * B, V).to(torch.float64), 1, generator=g)
         out["p"], out["q"] = p, q
+        out["target_logits"], out["draft_logits"] = zt, zd
         out["draft"] = draft.reshape(b, B).to(torch.int32).contiguous()
         out["u"] = torch.rand((b, B + 1), generator=g, dtype=torch.float32)
     return out

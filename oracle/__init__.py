@@ -20,6 +20,12 @@ Parity status of each function (what pins it, all in ``tests/test_oracle_*``):
                           position property, the copy rule.
   accept                  pinned: vocabulary-4 enumeration of acceptance and
                           residual laws, the lossless identity, special cases.
+  softmax_rows            pinned: scipy's softmax, closed forms (uniform and
+                          two-valued rows), exact shift and temperature
+                          identities, the limits of large and small T.
+  accept_logits           softmax_rows then accept (both pinned), plus the
+                          decision margins a differently rounded softmax may
+                          cross (ratio_boundary).
 """
 from __future__ import annotations
 
@@ -69,6 +75,8 @@ def _load():
         lib.simsd_oracle_rope_copy.restype = None
         lib.simsd_oracle_accept.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P]
         lib.simsd_oracle_accept.restype = None
+        lib.simsd_oracle_softmax_rows.argtypes = [P, I, I, D, P]
+        lib.simsd_oracle_softmax_rows.restype = None
         _lib = lib
     return _lib
 
@@ -203,4 +211,48 @@ def accept(p, q, draft, tau, u):
     _load().simsd_oracle_accept(_p(pp), _p(qq), _p(dr), _p(t), _p(uu), b, B, V,
                                 _p(out["accept_len"]), _p(out["correction"]), _p(out["status"]),
                                 _p(out["boundary"]))
+    return out
+
+
+def softmax_rows(z, temperature=1.0):
+    """Row softmax of fp32 logits at a temperature, fp64 arithmetic, fp32 out
+    (same shape as z; the last axis is the vocabulary)."""
+    zz = _f32(z)
+    V = zz.shape[-1]
+    rows = zz.size // V if V else 0
+    out = np.zeros_like(zz)
+    _load().simsd_oracle_softmax_rows(_p(zz), rows, V, float(temperature), _p(out))
+    return out
+
+
+def accept_logits(zt, zd, temperature, draft, tau, u, ratio_eps=4.0):
+    """Acceptance from target / draft logits: p = softmax(zt / T), q =
+    softmax(zd / T) (softmax_rows), then accept(p, q, ...). Adds
+    ratio_boundary[s] = 1 when an examined step's uniform lies within
+    ratio_eps fp32 ulps of its ratio min(1, p/q): a softmax rounded
+    differently in the last place may decide that step the other way."""
+    p = softmax_rows(zt, temperature)
+    q = softmax_rows(zd, temperature)
+    out = accept(p, q, draft, tau, u)
+    b, B, V = p.shape
+    tau_i = _i32(tau)
+    dr = _i32(draft)
+    uu = _f32(u)
+    rb = np.zeros(b, dtype=np.int32)
+    for s in range(b):
+        if out["status"][s] & 1:
+            continue
+        inv = np.argsort(tau_i[s])
+        L = int(out["accept_len"][s])
+        for t in range(min(L + 1, B)):
+            k = inv[t]
+            x = int(dr[s, k])
+            if x < 0 or x >= V:
+                continue
+            a, c = p[s, k, x], q[s, k, x]
+            r = np.float32(min(np.float32(1.0), a / c)) if c > 0 else np.float32(1.0 if a > 0 else 0.0)
+            if abs(float(uu[s, t]) - float(r)) <= ratio_eps * float(np.spacing(np.float32(max(r, 1e-30)))):
+                rb[s] = 1
+    out["ratio_boundary"] = rb
+    out["p"], out["q"] = p, q
     return out

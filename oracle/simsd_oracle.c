@@ -317,3 +317,26 @@ void simsd_oracle_accept(const float* p, const float* q, const int32_t* draft, c
   }
   free(inv);
 }
+
+/* Softmax of each row of logits at a sampling temperature, the distribution
+ * the target (and the draft) assign to each response position from the
+ * logits of its verification pass ([nl] Methodologie 4, Verificatie; [fr]
+ * Methodologie 4: the single forward pass yields the logits of every
+ * candidate). The temperature is this build's reading: the pages sample at
+ * temperature but do not define it for SimSD; p = softmax(z / T).
+ * Plain definition in fp64: m = max_y z_y (subtracting it changes nothing
+ * mathematically), s = sum_y exp((z_y - m) / T) in index order, and each
+ * output is exp((z_y - m) / T) / s rounded once to fp32 (the precision the
+ * acceptance decisions are taken in). */
+void simsd_oracle_softmax_rows(const float* z, int rows, int V, double temperature, float* out) {
+  for (int r = 0; r < rows; ++r) {
+    const float* zr = z + (size_t)r * V;
+    float* o = out + (size_t)r * V;
+    double m = -INFINITY;
+    for (int y = 0; y < V; ++y)
+      if ((double)zr[y] > m) m = (double)zr[y];
+    double s = 0.0;
+    for (int y = 0; y < V; ++y) s += exp(((double)zr[y] - m) / temperature);
+    for (int y = 0; y < V; ++y) o[y] = (float)(exp(((double)zr[y] - m) / temperature) / s);
+  }
+}
