@@ -232,6 +232,7 @@ def main():
     ws = binding.attention_workspace(dev, binding.simsd_verify_attention_workspace(
         b, B, Hq, Hkv, d, max_prefix))
     ws_acc = binding.accept_workspace(dev, binding.simsd_accept_workspace(b, B, w.V))
+    ws_accl = binding._cached_workspace("accept_logits", dev, binding.simsd_accept_logits_workspace(b, B, w.V))
     stream = torch.cuda.current_stream()
     lib = binding.load_library()
     P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
@@ -252,10 +253,13 @@ def main():
                  P(s["prefix_offsets"]), P(s["tau"]), P(s["start_pos"]), ctypes.c_float(w.rope_base), 0,
                  P(krots[j]), P(outs[j]), None, b, B, Hq, Hkv, d, max_prefix, ctypes.c_float(0.0),
                  binding.SIMSD_KV_HEAD_MAJOR, None, P(ws), ws.numel(), hs)
-        calls.append((rope, attn, acc, fused))
+        acc_logits = (P(s["target_logits"]), P(s["draft_logits"]), ctypes.c_float(1.0), P(s["draft"]),
+                      P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]), P(Cs[j]), None, P(ws_accl),
+                      ws_accl.numel(), hs)
+        calls.append((rope, attn, acc, fused, acc_logits))
 
     def step(i):
-        rope, attn, acc, _ = calls[i % len(calls)]
+        rope, attn, acc = calls[i % len(calls)][:3]
         rc = lib.simsd_rope_copy(*rope)
         rc |= lib.simsd_verify_attention(*attn)
         rc |= lib.simsd_accept(*acc)
@@ -263,7 +267,7 @@ def main():
             raise RuntimeError(f"libsimsd returned {rc}")
 
     def step_fused(i):
-        _, _, acc, fused = calls[i % len(calls)]
+        _, _, acc, fused = calls[i % len(calls)][:4]
         rc = lib.simsd_verify_attention_rope(*fused)
         rc |= lib.simsd_accept(*acc)
         if rc:
@@ -331,6 +335,7 @@ def main():
     fused_step_ms = f0.elapsed_time(f1) / args.steps
     attn_avg_s = alone(lib.simsd_verify_attention, 1)
     acc_us = alone(lib.simsd_accept, 2) * 1e6
+    acc_logits_us = alone(lib.simsd_accept_logits, 4) * 1e6
     rope_us = alone(lib.simsd_rope_copy, 0) * 1e6
     # spread of single steps: an event pair around each step
     pairs = [(ev(), ev()) for _ in range(min(args.steps, 200))]
@@ -373,7 +378,9 @@ def main():
                        "accept": round(acc_us, 3),
                        "step_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                        "fused_rope": {"verify_attention_rope": round(fused_us, 3),
-                                      "step": round(fused_step_ms * 1e3, 3)}},
+                                      "step": round(fused_step_ms * 1e3, 3)},
+                       "accept_logits": {"us": round(acc_logits_us, 3),
+                                         "logits_GBps": round(2 * b * B * w.V * 4 / acc_logits_us / 1e3, 1)}},
         "attention_mfma": {"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
                            "ceiling_at_hbm_peak": round(min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS), 4),
                            "flops_per_launch": flops},

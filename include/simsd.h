@@ -239,6 +239,43 @@ int simsd_accept(const float* p, const float* q, const int32_t* draft_tokens, co
 /* Workspace bytes simsd_accept needs for these sizes (0 on bad sizes). */
 size_t simsd_accept_workspace(int b, int B, int V);
 
+/*
+ * simsd_accept_logits -- acceptance from the verification logits ([nl]/[fr]
+ * Methodologie 4: the single verification pass yields the target's logits
+ * for every drafted position; the draft model's logits give q). The same
+ * decisions as simsd_accept on p = softmax(target_logits / T) and
+ * q = softmax(draft_logits / T), row-wise over the vocabulary, with the
+ * softmax evaluated where it is needed instead of materialised: one pass
+ * over all 2 b B rows finds each row's maximum and sum of exponentials
+ * (fp64), then the acceptance kernel evaluates p and q at the draft tokens
+ * and over the rejected position's row (fp64 exp, one rounding to fp32).
+ * The temperature is this library's reading (the pages do not define one for
+ * SimSD); T = 1 gives the plain softmax.
+ *
+ *   target_logits, draft_logits  fp32 [b][B][V], natural position order,
+ *                 16-byte aligned
+ *   temperature   T > 0, finite (else SIMSD_ERR_SCALE)
+ *   other arguments as for simsd_accept
+ *   workspace, ws_bytes  at least simsd_accept_logits_workspace() bytes,
+ *                 256-byte aligned, ALL ZERO before the first call that uses
+ *                 it (every call leaves its counters and ready words zero;
+ *                 the row statistics area is overwritten). Calls sharing a
+ *                 workspace must not run concurrently.
+ * Decisions agree with simsd_accept on the fp32-rounded softmax except where
+ * a uniform lies within a few fp32 ulps of its step's ratio, or u_{B+1} * Z
+ * within rounding of a CDF step (the exponentials are evaluated in another
+ * order than a sequential softmax).
+ * Errors: SIMSD_ERR_NULL, _SIZE (as simsd_accept; also 2 b B ceil(V/4096) >
+ * 2^24), _SCALE, _ALIGN, _WORKSPACE, _LAUNCH.
+ */
+int simsd_accept_logits(const float* target_logits, const float* draft_logits, float temperature,
+                        const int32_t* draft_tokens, const int32_t* tau, const float* uniforms, int b,
+                        int B, int V, int32_t* accept_len, int32_t* correction_token, int32_t* status,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes simsd_accept_logits needs (0 on bad sizes). */
+size_t simsd_accept_logits_workspace(int b, int B, int V);
+
 /* Static text for a simsd_status_t value. */
 const char* simsd_status_string(int code);
 

@@ -28,7 +28,8 @@ SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
 EXPORTS = (
     "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_rope",
     "simsd_verify_attention_workspace",
-    "simsd_accept", "simsd_accept_workspace", "simsd_status_string", "simsd_last_hip_error",
+    "simsd_accept", "simsd_accept_workspace", "simsd_accept_logits", "simsd_accept_logits_workspace",
+    "simsd_status_string", "simsd_last_hip_error",
 )
 
 
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_accept.restype = I
         lib.simsd_accept_workspace.argtypes = [I, I, I]
         lib.simsd_accept_workspace.restype = Z
+        lib.simsd_accept_logits.argtypes = [P, P, F, P, P, P, I, I, I, P, P, P, P, Z, P]
+        lib.simsd_accept_logits.restype = I
+        lib.simsd_accept_logits_workspace.argtypes = [I, I, I]
+        lib.simsd_accept_logits_workspace.restype = Z
         lib.simsd_status_string.argtypes = [I]
         lib.simsd_status_string.restype = ctypes.c_char_p
         lib.simsd_last_hip_error.argtypes = []
@@ -266,4 +271,39 @@ def simsd_accept(p, q, draft_tokens, tau, uniforms, accept_len=None, correction_
                                      workspace.numel() * workspace.element_size(),
                                      _stream(stream))
     _check("simsd_accept", rc)
+    return accept_len, correction_token
+
+
+def simsd_accept_logits_workspace(b: int, B: int, V: int) -> int:
+    return int(load_library().simsd_accept_logits_workspace(b, B, V))
+
+
+def simsd_accept_logits(target_logits, draft_logits, draft_tokens, tau, uniforms, temperature: float = 1.0,
+                        accept_len=None, correction_token=None, status=None, workspace=None, stream=None):
+    """Acceptance from fp32 logits [b][B][V] (softmax at `temperature`).
+    Returns (accept_len, correction_token), int32 [b]."""
+    _need(target_logits, "target_logits", torch.float32, 3)
+    _need(draft_logits, "draft_logits", torch.float32, 3)
+    _need(draft_tokens, "draft_tokens", torch.int32, 2)
+    _need(tau, "tau", torch.int32, 2)
+    _need(uniforms, "uniforms", torch.float32, 2)
+    b, B, V = target_logits.shape
+    if (tuple(draft_logits.shape) != (b, B, V) or tuple(draft_tokens.shape) != (b, B)
+            or tuple(tau.shape) != (b, B) or tuple(uniforms.shape) != (b, B + 1)):
+        raise ValueError("inconsistent shapes")
+    if accept_len is None:
+        accept_len = torch.empty(b, dtype=torch.int32, device=target_logits.device)
+    if correction_token is None:
+        correction_token = torch.empty(b, dtype=torch.int32, device=target_logits.device)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    need = simsd_accept_logits_workspace(b, B, V)
+    if workspace is None:
+        workspace = _cached_workspace("accept_logits", target_logits.device, need)
+    rc = load_library().simsd_accept_logits(_ptr(target_logits), _ptr(draft_logits), float(temperature),
+                                            _ptr(draft_tokens), _ptr(tau), _ptr(uniforms), b, B, V,
+                                            _ptr(accept_len), _ptr(correction_token), _ptr(status),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream))
+    _check("simsd_accept_logits", rc)
     return accept_len, correction_token

@@ -42,11 +42,56 @@ constexpr int kMaxSegments = kMaxAcceptVocab / (kAccThreads * kMinPer);
 constexpr unsigned long long kReady = 1ull << 63;
 constexpr int kPollLimit = 1 << 16;  // bound on the polls of one mass word
 
+// exp(x) for x <= 0 in fp64, relative error below 1e-14: Cody-Waite
+// reduction x = n ln2 + r with the two-part ln 2 of fdlibm (|r| <= ln2 / 2),
+// the Taylor series of e^r to degree 11 (truncation < 7e-15 there), and an
+// exponent scale by 2^n. Arguments below -708 give 0 (the softmax terms
+// they stand for are below fp64's normal range; the fp32 probabilities are 0).
+__device__ __forceinline__ double exp_nonpos(double x) {
+  const bool under = !(x > -708.0);  // branch-free: the result is selected at the end
+  x = under ? 0.0 : x;
+  const double n = rint(x * 1.4426950408889634);
+  double r = __builtin_fma(-n, 6.93147180369123816490e-01, x);
+  r = __builtin_fma(-n, 1.90821492927058770002e-10, r);
+  double e = 1.0 / 39916800.0;  // 1/11!
+  e = __builtin_fma(e, r, 1.0 / 3628800.0);
+  e = __builtin_fma(e, r, 1.0 / 362880.0);
+  e = __builtin_fma(e, r, 1.0 / 40320.0);
+  e = __builtin_fma(e, r, 1.0 / 5040.0);
+  e = __builtin_fma(e, r, 1.0 / 720.0);
+  e = __builtin_fma(e, r, 1.0 / 120.0);
+  e = __builtin_fma(e, r, 1.0 / 24.0);
+  e = __builtin_fma(e, r, 1.0 / 6.0);
+  e = __builtin_fma(e, r, 0.5);
+  e = __builtin_fma(e, r, 1.0);
+  e = __builtin_fma(e, r, 1.0);
+  return under ? 0.0 : ldexp(e, static_cast<int>(n));
+}
+
+// Softmax probability of logit z in a row with statistics (max m, sum of
+// exp s, passed as 1/s) at inverse temperature inv_t: exp((z - m) inv_t) / s
+// in fp64, rounded once to fp32 (the precision the decisions are taken in).
+__device__ __forceinline__ float softmax_prob(float z, double m, double inv_s, double inv_t) {
+  return static_cast<float>(exp_nonpos((static_cast<double>(z) - m) * inv_t) * inv_s);
+}
+
+// Row statistics of the target and draft rows (s, k): (max, 1 / sum of exp).
+struct RowStats {
+  double mt, st, md, sd;  // st, sd: reciprocal row sums
+};
+__device__ __forceinline__ RowStats row_stats_of(const AcceptArgs& a, int s, int k) {
+  const size_t rt = static_cast<size_t>(s) * a.B + k, rd = rt + static_cast<size_t>(a.b) * a.B;
+  // the statistics pass stores (max, 1 / sum)
+  return RowStats{a.row_stats[2 * rt], a.row_stats[2 * rt + 1], a.row_stats[2 * rd], a.row_stats[2 * rd + 1]};
+}
+
 // Masses of entries y0 .. y0+PER-1 of one row: the residual max(0, p - q) in
 // fp32, or p itself for the zero-residual fallback; entries at or past V are 0.
-template <int PER>
+// LOGITS: prow / qrow are logits rows and p, q their softmax (row stats rs).
+template <int PER, bool LOGITS>
 __device__ __forceinline__ void load_masses(const float* prow, const float* qrow, int y0, int V,
-                                            bool vec, bool use_p, float (&w)[PER]) {
+                                            bool vec, bool use_p, const RowStats& rs, double inv_t,
+                                            float (&w)[PER]) {
   float pv[PER], qv[PER];
   if (vec && y0 + PER <= V) {
 #pragma unroll
@@ -60,8 +105,15 @@ __device__ __forceinline__ void load_masses(const float* prow, const float* qrow
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const bool in = y0 + e < V;
-      pv[e] = in ? prow[y0 + e] : 0.0f;
-      qv[e] = (in && !use_p) ? qrow[y0 + e] : 0.0f;
+      pv[e] = in ? prow[y0 + e] : (LOGITS ? -INFINITY : 0.0f);
+      qv[e] = (in && !use_p) ? qrow[y0 + e] : (LOGITS ? -INFINITY : 0.0f);
+    }
+  }
+  if constexpr (LOGITS) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      pv[e] = softmax_prob(pv[e], rs.mt, rs.st, inv_t);
+      qv[e] = use_p ? 0.0f : softmax_prob(qv[e], rs.md, rs.sd, inv_t);
     }
   }
 #pragma unroll
@@ -169,7 +221,7 @@ __device__ int locate_segment(const double* m, int nseg, float u, int* seg_out, 
   return 1;
 }
 
-template <int PER>
+template <int PER, bool LOGITS>
 __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   constexpr int kSeg = kAccThreads * PER;  // entries per segment / workgroup
   __shared__ int inv_s[64];
@@ -211,7 +263,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
           r = 0.0f;
         } else {
           const size_t at = (static_cast<size_t>(s) * B + kk) * V + x;
-          const float pa = a.p[at], qa = a.q[at];
+          float pa, qa;
+          if constexpr (LOGITS) {
+            const RowStats rs = row_stats_of(a, s, kk);
+            pa = softmax_prob(a.zt[at], rs.mt, rs.st, a.inv_t);
+            qa = softmax_prob(a.zd[at], rs.md, rs.sd, a.inv_t);
+          } else {
+            pa = a.p[at], qa = a.q[at];
+          }
           if (qa > 0.0f) {
             r = pa / qa;  // IEEE-rounded fp32 division (no fast-math in this library)
             r = r > 1.0f ? 1.0f : r;
@@ -247,14 +306,16 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   }
 
   const int kstar = inv_s[L];
-  const float* prow = a.p + (static_cast<size_t>(s) * B + kstar) * V;
-  const float* qrow = a.q + (static_cast<size_t>(s) * B + kstar) * V;
+  const float* prow = (LOGITS ? a.zt : a.p) + (static_cast<size_t>(s) * B + kstar) * V;
+  const float* qrow = (LOGITS ? a.zd : a.q) + (static_cast<size_t>(s) * B + kstar) * V;
   const bool vec = (V % 4) == 0;
+  RowStats rs{};
+  if constexpr (LOGITS) rs = row_stats_of(a, s, kstar);
 
   // ---- every workgroup: residual mass of its segment, published with the
   // ready bit; the arrival counter moves without waiting for the publish ----
   float w[PER];
-  load_masses<PER>(prow, qrow, seg * kSeg + PER * tid, V, vec, false, w);
+  load_masses<PER, LOGITS>(prow, qrow, seg * kSeg + PER * tid, V, vec, false, rs, a.inv_t, w);
   const double mine = block_sum(thread_sum<PER>(w));
   unsigned long long* words = reinterpret_cast<unsigned long long*>(a.seg_sum) +
                               static_cast<size_t>(s) * nseg;
@@ -297,7 +358,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     if (use_p) {  // zero residual: the (rare) fallback draws from p; masses of p, all segments here
       for (int j = 0; j < nseg; ++j) {
         float wp[PER];
-        load_masses<PER>(prow, qrow, j * kSeg + PER * tid, V, vec, true, wp);
+        load_masses<PER, LOGITS>(prow, qrow, j * kSeg + PER * tid, V, vec, true, rs, a.inv_t, wp);
         const double m = block_sum(thread_sum<PER>(wp));
         if (tid == 0) sh_mass[j] = m;
       }
@@ -327,7 +388,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   const int j = sh_seg;  // < 0: no mass anywhere
   if (j >= 0) {
     const int y0 = j * kSeg + PER * tid;
-    if (j != seg || use_p) load_masses<PER>(prow, qrow, y0, V, vec, use_p, w);
+    if (j != seg || use_p) load_masses<PER, LOGITS>(prow, qrow, y0, V, vec, use_p, rs, a.inv_t, w);
     double total;
     const double excl = block_excl_scan(thread_sum<PER>(w), &total);
     const double T = sh_T, base = sh_base;
@@ -362,6 +423,130 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   }
 }
 
+// Maximum of one float per thread over the workgroup, returned to every thread.
+__device__ float block_max_all(float v) {
+  __shared__ float sh_wave[kAccWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  if (lane == 0) sh_wave[wave] = v;
+  __syncthreads();
+  float m = sh_wave[0];
+  for (int w = 1; w < kAccWaves; ++w) m = fmaxf(m, sh_wave[w]);
+  __syncthreads();
+  return m;
+}
+
+// Row statistics for acceptance from logits: for every target and draft row
+// (2 b B rows of V logits) the maximum m and s = sum_y exp((z_y - m) / T).
+// Grid: rows x segments of 256 PER1 entries (PER1 per thread). Each
+// workgroup reduces its segment to (m_j, s_j) -- s_j relative to its own
+// maximum -- and publishes both with ready bits; the row's last arrival
+// collects them, folds S = sum_j s_j exp((m_j - M) / T) with M = max_j m_j in a
+// fixed order, writes (M, S) and clears its words and counter.
+template <int PER1>
+__global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
+  constexpr int SEG1 = PER1 * kAccThreads;
+  __shared__ int sh_last;
+  const int nrow_half = a.b * a.B;
+  const long id = blockIdx.x;
+  const int row = static_cast<int>(id / a.nseg1), seg = static_cast<int>(id % a.nseg1);
+  const int V = a.V, tid = threadIdx.x;
+  const float* z = (row < nrow_half ? a.zt : a.zd) + static_cast<size_t>(row % nrow_half) * V;
+  const int y0 = seg * SEG1 + PER1 * tid;
+  float v[PER1];
+  if ((V % 4) == 0 && y0 + PER1 <= V) {
+#pragma unroll
+    for (int j = 0; j < PER1 / 4; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(z + y0 + 4 * j);
+      v[4 * j] = f.x, v[4 * j + 1] = f.y, v[4 * j + 2] = f.z, v[4 * j + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER1; ++e) v[e] = y0 + e < V ? z[y0 + e] : -INFINITY;
+  }
+  float tm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PER1; ++e) tm = fmaxf(tm, v[e]);
+  const float m = block_max_all(tm);
+  double ts = 0.0;
+#pragma unroll
+  for (int e = 0; e < PER1; ++e) ts += exp_nonpos((static_cast<double>(v[e]) - static_cast<double>(m)) * a.inv_t);
+  const double sum = block_sum(ts);
+
+  unsigned long long* words = a.row_words + static_cast<size_t>(row) * a.nseg1 * 2;
+  if (tid == 0) {
+    __hip_atomic_store(words + 2 * seg, static_cast<unsigned long long>(__float_as_uint(m)) | kReady,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(words + 2 * seg + 1,
+                       static_cast<unsigned long long>(__double_as_longlong(sum)) | kReady, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    const int prev = __hip_atomic_fetch_add(&a.row_counters[row], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = prev == a.nseg1 - 1;
+  }
+  __syncthreads();
+  if (!sh_last) return;
+
+  // last arrival: every thread collects its segments (in order), clearing the
+  // words it read (its own were published by thread 0, which clears them)
+  constexpr int kMaxSegPerThread = (kMaxAcceptVocab / SEG1 + kAccThreads - 1) / kAccThreads;
+  float mj[kMaxSegPerThread];
+  double sj[kMaxSegPerThread];
+  float tmax = -INFINITY;
+  bool timed_out = false;
+#pragma unroll
+  for (int i = 0; i < kMaxSegPerThread; ++i) {
+    const int j = tid + i * kAccThreads;
+    mj[i] = -INFINITY;
+    sj[i] = 0.0;
+    if (j >= a.nseg1) continue;
+    if (j == seg) {
+      mj[i] = m;
+      sj[i] = sum;  // thread 0 holds the block sum; broadcast below
+      continue;
+    }
+    unsigned long long wm = 0, ws = 0;
+    int polls = 0;
+    do {
+      wm = __hip_atomic_load(words + 2 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ws = __hip_atomic_load(words + 2 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((wm & kReady) && (ws & kReady)) break;
+      __builtin_amdgcn_s_sleep(1);
+    } while (++polls < kPollLimit);
+    timed_out |= !((wm & kReady) && (ws & kReady));
+    mj[i] = __uint_as_float(static_cast<uint32_t>(wm));
+    sj[i] = __longlong_as_double(static_cast<long long>(ws & ~kReady));
+    __hip_atomic_store(words + 2 * j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(words + 2 * j + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the own segment's sum lives in thread 0 (block_sum); hand it to its owner
+  __shared__ double sh_own;
+  if (tid == 0) {
+    sh_own = sum;
+    __hip_atomic_store(words + 2 * seg, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(words + 2 * seg + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMaxSegPerThread; ++i) {
+    if (tid + i * kAccThreads == seg) sj[i] = sh_own;
+    tmax = fmaxf(tmax, mj[i]);
+  }
+  const float M = block_max_all(tmax);
+  double part = 0.0;
+#pragma unroll
+  for (int i = 0; i < kMaxSegPerThread; ++i)
+    if (tid + i * kAccThreads < a.nseg1)
+      part += sj[i] * exp_nonpos((static_cast<double>(mj[i]) - static_cast<double>(M)) * a.inv_t);
+  const double S = block_sum(part);
+  if (timed_out && a.status) atomicOr(&a.status[(row % nrow_half) / a.B], kDevSyncTimeout);
+  if (tid == 0) {
+    a.row_stats[2 * static_cast<size_t>(row)] = static_cast<double>(M);
+    a.row_stats[2 * static_cast<size_t>(row) + 1] = 1.0 / S;
+    __hip_atomic_store(&a.row_counters[row], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Entries per thread (segment width / 256). SIMSD_ACCEPT_PER = 4, 8 or 16
 // overrides the default (read on every call).
 int accept_per(int b, int V) {
@@ -377,17 +562,45 @@ int accept_per(int b, int V) {
 
 int accept_segments(int V) { return (V + kAccThreads * kMinPer - 1) / (kAccThreads * kMinPer); }
 
-hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
+template <bool LOGITS>
+hipError_t launch_accept_mode(const AcceptArgs& a, hipStream_t stream) {
   const int per = accept_per(a.b, a.V);
   const int nseg = (a.V + kAccThreads * per - 1) / (kAccThreads * per);
   dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(a.b));
   if (per == 4)
-    hipLaunchKernelGGL(accept_kernel<4>, grid, dim3(kAccThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_kernel<4, LOGITS>), grid, dim3(kAccThreads), 0, stream, a);
   else if (per == 8)
-    hipLaunchKernelGGL(accept_kernel<8>, grid, dim3(kAccThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_kernel<8, LOGITS>), grid, dim3(kAccThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(accept_kernel<16>, grid, dim3(kAccThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_kernel<16, LOGITS>), grid, dim3(kAccThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) { return launch_accept_mode<false>(a, stream); }
+
+// Entries per thread of the row-statistics pass: SIMSD_ROWSTAT_PER = 16, 32
+// or 64 overrides the default (read on every call).
+int row_stat_per() {
+  const char* e = getenv("SIMSD_ROWSTAT_PER");
+  const int forced = e ? atoi(e) : 0;
+  return (forced == 16 || forced == 32 || forced == 64) ? forced : 32;
+}
+
+hipError_t launch_accept_logits(const AcceptArgs& a0, hipStream_t stream) {
+  AcceptArgs a = a0;
+  const int per1 = row_stat_per();
+  a.nseg1 = (a.V + kAccThreads * per1 - 1) / (kAccThreads * per1);
+  const long units = 2L * a.b * a.B * a.nseg1;
+  const dim3 grid(static_cast<unsigned>(units)), block(kAccThreads);
+  if (per1 == 16)
+    hipLaunchKernelGGL(row_stats_kernel<16>, grid, block, 0, stream, a);
+  else if (per1 == 32)
+    hipLaunchKernelGGL(row_stats_kernel<32>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(row_stats_kernel<64>, grid, block, 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_accept_mode<true>(a, stream);
 }
 
 }  // namespace simsd

@@ -208,6 +208,54 @@ int simsd_accept(const float* p, const float* q, const int32_t* draft_tokens, co
   return launch_status(simsd::launch_accept(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t simsd_accept_logits_workspace(int b, int B, int V) {
+  const size_t base = simsd_accept_workspace(b, B, V);
+  if (!base) return 0;
+  const long rows = 2L * b * B;
+  const long nseg1 = (V + simsd::kRowStatSeg - 1) / simsd::kRowStatSeg;
+  if (rows * nseg1 > simsd::kMaxRowStatUnits) return 0;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return base + up(rows * sizeof(int32_t)) + up(rows * nseg1 * 2 * sizeof(uint64_t)) +
+         up(rows * 2 * sizeof(double));
+}
+
+int simsd_accept_logits(const float* target_logits, const float* draft_logits, float temperature,
+                        const int32_t* draft_tokens, const int32_t* tau, const float* uniforms, int b,
+                        int B, int V, int32_t* accept_len, int32_t* correction_token, int32_t* status,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !draft_tokens || !tau || !uniforms || !accept_len ||
+      !correction_token)
+    return SIMSD_ERR_NULL;
+  if (b < 1 || b > simsd::kMaxSeqCounters || B < 1 || B > 64 || V < 1 || V > simsd::kMaxAcceptVocab)
+    return SIMSD_ERR_SIZE;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SIMSD_ERR_SCALE;
+  if (!aligned16(target_logits) || !aligned16(draft_logits)) return SIMSD_ERR_ALIGN;
+  const size_t need = simsd_accept_logits_workspace(b, B, V);
+  if (!need) return SIMSD_ERR_SIZE;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || ws_bytes < need)
+    return SIMSD_ERR_WORKSPACE;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const long rows = 2L * b * B;
+  const int nseg1 = (V + simsd::kRowStatSeg - 1) / simsd::kRowStatSeg;
+  char* ws = static_cast<char*>(workspace);
+  const size_t acc_bytes = simsd_accept_workspace(b, B, V);
+  simsd::AcceptArgs a{};
+  a.zt = target_logits, a.zd = draft_logits, a.draft = draft_tokens, a.tau = tau, a.u = uniforms;
+  a.b = b, a.B = B, a.V = V;
+  a.accept_len = accept_len, a.correction = correction_token, a.status = status;
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.seg_sum = reinterpret_cast<double*>(ws + static_cast<size_t>(simsd::kMaxSeqCounters) * sizeof(int32_t));
+  size_t off = acc_bytes;
+  a.row_counters = reinterpret_cast<int32_t*>(ws + off);
+  off += up(rows * sizeof(int32_t));
+  a.row_words = reinterpret_cast<unsigned long long*>(ws + off);
+  off += up(rows * nseg1 * 2 * sizeof(uint64_t));
+  a.row_stats = reinterpret_cast<double*>(ws + off);
+  a.nseg1 = nseg1;
+  a.inv_t = 1.0 / static_cast<double>(temperature);
+  return launch_status(simsd::launch_accept_logits(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* simsd_status_string(int code) {
   switch (code) {
     case SIMSD_OK: return "ok";

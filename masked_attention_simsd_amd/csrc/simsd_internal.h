@@ -133,6 +133,16 @@ struct AcceptArgs {
   int32_t* status;
   int32_t* counters;  // [b], zero between calls
   double* seg_sum;    // [b][segments] published residual mass words (ready bit), zero between calls
+  // Logits input (simsd_accept_logits): p and q are the row softmaxes of zt
+  // and zd at temperature 1 / inv_t, evaluated where needed from the row
+  // statistics (max, sum of exp) the row-statistics pass leaves in row_stats.
+  const float* zt;
+  const float* zd;
+  double* row_stats;              // [2][b][B] x (max, 1 / sum): target rows, then draft rows
+  double inv_t;
+  int32_t* row_counters;          // [2 b B], zero between calls
+  unsigned long long* row_words;  // [2 b B][nseg1] x (max, sum) with ready bits, zero between calls
+  int nseg1;                      // vocabulary segments per row of the statistics pass
 };
 
 int accept_segments(int V);
@@ -149,5 +159,10 @@ AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, in
 hipError_t launch_rope_copy(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_verify_attention(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+// acceptance from logits: the row-statistics pass, then the acceptance kernel
+// in logits mode (same stream)
+hipError_t launch_accept_logits(const AcceptArgs& a, hipStream_t stream);
+constexpr int kRowStatSeg = 4096;  // smallest statistics segment (sizes the workspace)
+constexpr long kMaxRowStatUnits = 1L << 24;  // rows x segments of one statistics pass
 
 }  // namespace simsd

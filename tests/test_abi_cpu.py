@@ -151,3 +151,23 @@ def test_accept_host_errors(lib):
     assert f(ws=None) == 6
     assert f(ws=MISALIGNED) == 6
     assert f(wsb=lib.simsd_accept_workspace(1, 4, 16) - 1) == 6
+
+
+def test_accept_logits_host_errors(lib):
+    f = lambda **kw: lib.simsd_accept_logits(kw.get("zt", FAKE), kw.get("zd", FAKE), kw.get("T", 1.0), FAKE,
+                                             FAKE, FAKE, kw.get("b", 1), kw.get("B", 4), kw.get("V", 16),
+                                             kw.get("L", FAKE), FAKE, None, kw.get("ws", FAKE),
+                                             kw.get("wsb", 1 << 30), None)
+    assert f(zt=None) == 1
+    assert f(L=None) == 1
+    assert f(b=0) == 2
+    assert f(B=65) == 2
+    assert f(V=(1 << 21) + 1) == 2
+    assert f(T=0.0) == 9
+    assert f(T=float("inf")) == 9
+    assert f(zd=MISALIGNED) == 7
+    assert f(ws=None) == 6
+    assert f(wsb=lib.simsd_accept_logits_workspace(1, 4, 16) - 1) == 6
+    n = lib.simsd_accept_logits_workspace(8, 16, 151936)
+    assert n > lib.simsd_accept_workspace(8, 16, 151936) and n % 256 == 0
+    assert lib.simsd_accept_logits_workspace(65536, 64, 1 << 21) == 0  # statistics units over 2^24
