@@ -691,7 +691,12 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     // barrier waits for this workgroup's stores to be acknowledged before the
     // counter is bumped, and the last workgroup reads only after its bump
     // returned.
-    constexpr int PART_O_B = NWC * QB * DB * 64 * 16;  // bytes of one split's O partial
+    // With a bf16 output the unnormalised O partials travel as bf16 (one more
+    // rounding of relative size 2^-9, below the output's own), halving the
+    // hand-off and merge bytes; with an fp32 output they stay fp32.
+    constexpr bool PBF = !OUT_F32;
+    constexpr int EB = PBF ? 8 : 16;                    // bytes per lane and (row block, d block)
+    constexpr int PART_O_B = NWC * QB * DB * 64 * EB;   // bytes of one split's O partial
     constexpr int PART_ML_B = MWG * 8;                  // bytes of one split's (m, l) pairs
     const size_t part = static_cast<size_t>(us) * a.nsplit + split;
     if (owner) {
@@ -699,9 +704,15 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[qb][db]), ro,
-                                                 (((rw * QB + qb) * DB + db) * 64 + lane) * 16, 0, kCoherent);
+        for (int db = 0; db < DB; ++db) {
+          const int off = (((rw * QB + qb) * DB + db) * 64 + lane) * EB;
+          if constexpr (PBF)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{pack_bf16x2(oacc[qb][db][0], oacc[qb][db][1]), pack_bf16x2(oacc[qb][db][2], oacc[qb][db][3])},
+                ro, off, 0, kCoherent);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[qb][db]), ro, off, 0, kCoherent);
+        }
       if (a16 == 0) {
         const auto rml = coherent_rsrc(reinterpret_cast<char*>(a.part_ml) + part * PART_ML_B, PART_ML_B);
 #pragma unroll
@@ -723,7 +734,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
       // Online log-sum-exp merge of the ns partials in split order (fixed, so
       // the result does not depend on which workgroup came last). The loads of
       // MB partials are issued together: one memory round trip per MB splits.
-      constexpr int MB = QB == 1 ? 4 : 2;
+      constexpr int MB = (QB == 1 || PBF) ? 4 : 2;
       const size_t part0 = static_cast<size_t>(us) * a.nsplit;
       const auto ro = coherent_rsrc(reinterpret_cast<char*>(a.part_o) + part0 * PART_O_B, ns * PART_O_B);
       const auto rml = coherent_rsrc(reinterpret_cast<char*>(a.part_ml) + part0 * PART_ML_B, ns * PART_ML_B);
@@ -747,10 +758,17 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
             ml[j][qb] = __builtin_bit_cast(
                 f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, k * PART_ML_B + row * 8, 0, kCoherent));
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-              po[j][qb][db] = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                             ro, k * PART_O_B + (((rw * QB + qb) * DB + db) * 64 + lane) * 16, 0, kCoherent));
+            for (int db = 0; db < DB; ++db) {
+              const int off = k * PART_O_B + (((rw * QB + qb) * DB + db) * 64 + lane) * EB;
+              if constexpr (PBF) {
+                const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, kCoherent));
+                po[j][qb][db] = f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xffff0000u),
+                                      __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xffff0000u)};
+              } else {
+                po[j][qb][db] =
+                    __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, kCoherent));
+              }
+            }
           }
         }
 #pragma unroll
