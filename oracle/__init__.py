@@ -20,6 +20,9 @@ Parity status of each function (what pins it, all in ``tests/test_oracle_*``):
                           position property, the copy rule.
   accept                  pinned: vocabulary-4 enumeration of acceptance and
                           residual laws, the lossless identity, special cases.
+  attention_masked        pinned: equals verify_attention bit for bit on the
+                          tau-derived mask; numpy softmax attention over
+                          explicitly gathered keys for random masks; empty rows.
   softmax_rows            pinned: scipy's softmax, closed forms (uniform and
                           two-valued rows), exact shift and temperature
                           identities, the limits of large and small T.
@@ -77,6 +80,8 @@ def _load():
         lib.simsd_oracle_accept.restype = None
         lib.simsd_oracle_softmax_rows.argtypes = [P, I, I, D, P]
         lib.simsd_oracle_softmax_rows.restype = None
+        lib.simsd_oracle_attention_masked.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, D, P, P]
+        lib.simsd_oracle_attention_masked.restype = None
         _lib = lib
     return _lib
 
@@ -256,3 +261,22 @@ def accept_logits(zt, zd, temperature, draft, tau, u, ratio_eps=4.0):
     out["ratio_boundary"] = rb
     out["p"], out["q"] = p, q
     return out
+
+
+def attention_masked(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, allowed, scale=None):
+    """Block rows under an explicit mask: allowed [b][R][R] (bool; row r may
+    see block key c), plus the whole cached prefix. Returns (out, lse) fp64;
+    rows with no visible key give out 0, lse -inf."""
+    q, kb, vb = _f64(q_blk), _f64(k_blk), _f64(v_blk)
+    kp, vp = _f64(k_pre), _f64(v_pre)
+    off = _i32(prefix_offsets)
+    al = np.ascontiguousarray(np.asarray(allowed, dtype=np.uint8))
+    b, R, Hq, d = q.shape
+    Hkv = kb.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros(q.shape)
+    lse = np.zeros((b, R, Hq))
+    _load().simsd_oracle_attention_masked(_p(q), _p(kb), _p(vb), _p(kp), _p(vp), _p(off), _p(al), b, R,
+                                          Hq, Hkv, d, float(scale), _p(out), _p(lse))
+    return out, lse

@@ -340,3 +340,74 @@ void simsd_oracle_softmax_rows(const float* z, int rows, int V, double temperatu
     for (int y = 0; y < V; ++y) o[y] = (float)(exp(((double)zr[y] - m) / temperature) / s);
   }
 }
+
+/* Attention of block rows under an explicit block mask instead of the
+ * temporal rule: the "next" generalisation the SimSD pages point to for
+ * verifying several drafts or a draft graph against one cached prefix
+ * (Spiffy page, draft graphs; [nl]/[fr] Methodologie 2 is the special case
+ * the tau rule produces). Every row sees the whole cached prefix of its
+ * sequence and the block keys c with allowed[s][r][c] != 0; the softmax runs
+ * over those keys only (fp64, keys in order prefix 0..P-1 then block rows
+ * 0..R-1, exactly as simsd_oracle_attention_row). A row with no visible key
+ * (empty prefix and no allowed block key) has out = 0 and lse = -inf.
+ *   q_blk [b][R][Hq][d], k_blk/v_blk [b][R][Hkv][d], allowed [b][R][R] bytes,
+ *   k_pre/v_pre packed [sum P][Hkv][d] with prefix_offsets[b+1];
+ *   out [b][R][Hq][d], lse [b][R][Hq]. */
+void simsd_oracle_attention_masked(const double* q_blk, const double* k_blk, const double* v_blk,
+                                   const double* k_pre, const double* v_pre,
+                                   const int32_t* prefix_offsets, const uint8_t* allowed, int b, int R,
+                                   int Hq, int Hkv, int d, double scale, double* out, double* lse) {
+  int G = Hq / Hkv;
+  for (int s = 0; s < b; ++s) {
+    int P = prefix_offsets[s + 1] - prefix_offsets[s];
+    const double* kp = k_pre + (size_t)prefix_offsets[s] * Hkv * d;
+    const double* vp = v_pre + (size_t)prefix_offsets[s] * Hkv * d;
+    const double* kb = k_blk + (size_t)s * R * Hkv * d;
+    const double* vb = v_blk + (size_t)s * R * Hkv * d;
+    int nkeys = P + R;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)nkeys);
+    char* ok = (char*)malloc((size_t)nkeys);
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* arow = allowed + ((size_t)s * R + r) * R;
+      for (int h = 0; h < Hq; ++h) {
+        size_t row = ((size_t)s * R + r) * Hq + h;
+        const double* q = q_blk + row * d;
+        int g = h / G;
+        double m = -INFINITY;
+        for (int j = 0; j < nkeys; ++j) {
+          const double* kj;
+          if (j < P) {
+            ok[j] = 1;
+            kj = kp + ((size_t)j * Hkv + g) * d;
+          } else {
+            ok[j] = (char)(arow[j - P] != 0);
+            kj = kb + ((size_t)(j - P) * Hkv + g) * d;
+          }
+          if (!ok[j]) continue;
+          double dot = 0.0;
+          for (int e = 0; e < d; ++e) dot += q[e] * kj[e];
+          sc[j] = dot * scale;
+          if (sc[j] > m) m = sc[j];
+        }
+        double* o = out + row * d;
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        if (m == -INFINITY) {
+          lse[row] = -INFINITY;
+          continue;
+        }
+        double denom = 0.0;
+        for (int j = 0; j < nkeys; ++j) {
+          if (!ok[j]) continue;
+          double w = exp(sc[j] - m);
+          denom += w;
+          const double* vj = j < P ? vp + ((size_t)j * Hkv + g) * d : vb + ((size_t)(j - P) * Hkv + g) * d;
+          for (int e = 0; e < d; ++e) o[e] += w * vj[e];
+        }
+        for (int e = 0; e < d; ++e) o[e] /= denom;
+        lse[row] = m + log(denom);
+      }
+    }
+    free(sc);
+    free(ok);
+  }
+}
