@@ -16,7 +16,8 @@
  * attention pass under the temporal mask (Methodologie 2), and finally the
  * drafts are accepted or rejected along the draft's temporal order. The entry
  * points below are the attention-layer and acceptance parts of that step
- * (RoPE-copy, attention, acceptance, and RoPE-copy fused into attention);
+ * (RoPE-copy, attention, acceptance), and their extensions (RoPE-copy fused
+ * into attention, attention under an explicit mask, acceptance from logits);
  * projections, MLP and LM head are outside this library.
  *
  * Conventions common to every entry point
@@ -164,6 +165,35 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
 /* Workspace bytes simsd_verify_attention (and simsd_verify_attention_rope)
  * needs for these sizes (0 on bad sizes). */
 size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix);
+
+/*
+ * simsd_verify_attention_mask -- the same attention pass with the block mask
+ * given explicitly instead of generated from tau: the generalisation that
+ * verifies several drafts or a draft graph against one cached prefix (the
+ * Spiffy page's draft graphs; the tau rule of [nl]/[fr] Methodologie 2 is the
+ * special case). Every block row sees the whole cached prefix of its sequence
+ * and the block keys its mask allows; the softmax runs over those keys only.
+ * A row that sees no key (empty prefix, empty mask row) gets out = 0 and
+ * lse = -inf.
+ *
+ *   q_blk, k_blk, v_blk  bf16 [b][R][Hq|Hkv|Hkv][d], R block rows (1..128)
+ *   block_mask   uint64 [b][R][ceil(R/64)], 8-byte aligned: bit (c % 64) of
+ *                word c / 64 of row r set = row r sees block key c
+ *   flags        SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR only
+ *   status       optional int32 [b]; SIMSD_DEV_BAD_PREFIX
+ *   other arguments as for simsd_verify_attention; the workspace size comes
+ *   from simsd_verify_attention_mask_workspace.
+ * Errors: SIMSD_ERR_NULL, _SIZE (R outside 1..128, ...), _HEADS, _HEAD_DIM,
+ * _FLAGS, _WORKSPACE, _ALIGN, _SCALE, _LAUNCH.
+ */
+int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
+                                const void* v_pre, const int32_t* prefix_offsets, const uint64_t* block_mask,
+                                void* out, float* lse, int b, int R, int Hq, int Hkv, int d, int max_prefix,
+                                float scale, uint32_t flags, int32_t* status, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/* Workspace bytes simsd_verify_attention_mask needs (0 on bad sizes). */
+size_t simsd_verify_attention_mask_workspace(int b, int R, int Hq, int Hkv, int d, int max_prefix);
 
 /*
  * simsd_verify_attention_rope -- the RoPE copy rule ([nl]/[fr] Methodologie

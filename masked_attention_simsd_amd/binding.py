@@ -27,7 +27,8 @@ SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
 
 EXPORTS = (
     "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_rope",
-    "simsd_verify_attention_workspace",
+    "simsd_verify_attention_workspace", "simsd_verify_attention_mask",
+    "simsd_verify_attention_mask_workspace",
     "simsd_accept", "simsd_accept_workspace", "simsd_accept_logits", "simsd_accept_logits_workspace",
     "simsd_status_string", "simsd_last_hip_error",
 )
@@ -62,6 +63,10 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_verify_attention_rope.restype = I
         lib.simsd_verify_attention_workspace.argtypes = [I, I, I, I, I, I]
         lib.simsd_verify_attention_workspace.restype = Z
+        lib.simsd_verify_attention_mask.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, U, P, P, Z, P]
+        lib.simsd_verify_attention_mask.restype = I
+        lib.simsd_verify_attention_mask_workspace.argtypes = [I, I, I, I, I, I]
+        lib.simsd_verify_attention_mask_workspace.restype = Z
         lib.simsd_accept.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P, Z, P]
         lib.simsd_accept.restype = I
         lib.simsd_accept_workspace.argtypes = [I, I, I]
@@ -239,6 +244,53 @@ def _attention(fn, q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, 
         start_pos, base, rflags, k_rot = rope
         rc = lib.simsd_verify_attention_rope(*head, _ptr(start_pos), base, rflags, _ptr(k_rot), *tail)
     _check(fn, rc)
+    return out
+
+
+def simsd_verify_attention_mask_workspace(b: int, R: int, Hq: int, Hkv: int, d: int, max_prefix: int) -> int:
+    return int(load_library().simsd_verify_attention_mask_workspace(b, R, Hq, Hkv, d, max_prefix))
+
+
+def simsd_verify_attention_mask(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, block_mask, out=None,
+                                lse=None, max_prefix: int | None = None, scale: float = 0.0, flags: int = 0,
+                                status=None, workspace=None, stream=None):
+    """Attention of R block rows under an explicit block mask: block_mask is an
+    int64 tensor [b][R][ceil(R/64)] holding the uint64 bit words (bit c % 64 of
+    word c // 64 of row r: row r sees block key c). Returns out."""
+    for t, n in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk")):
+        _need(t, n, torch.bfloat16, 4)
+    for t, n in ((k_pre, "k_pre"), (v_pre, "v_pre")):
+        _need(t, n, torch.bfloat16, 3)
+    _need(prefix_offsets, "prefix_offsets", torch.int32, 1)
+    _need(block_mask, "block_mask", torch.int64, 3)
+    b, R, Hq, d = q_blk.shape
+    Hkv = k_blk.shape[2]
+    head_major = bool(flags & SIMSD_KV_HEAD_MAJOR)
+    pre_ok = (k_pre.shape[0] == Hkv and k_pre.shape[2] == d) if head_major else k_pre.shape[1:] == (Hkv, d)
+    if (tuple(k_blk.shape) != (b, R, Hkv, d) or tuple(v_blk.shape) != (b, R, Hkv, d) or not pre_ok
+            or v_pre.shape != k_pre.shape or prefix_offsets.shape[0] != b + 1
+            or tuple(block_mask.shape) != (b, R, (R + 63) // 64)):
+        raise ValueError("inconsistent shapes")
+    if max_prefix is None:
+        off = prefix_offsets.cpu()
+        max_prefix = int((off[1:] - off[:-1]).max()) if b > 0 else 0
+    out_f32 = bool(flags & SIMSD_OUT_F32)
+    if out is None:
+        out = torch.empty_like(q_blk, dtype=torch.float32 if out_f32 else torch.bfloat16)
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, 4)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    need = simsd_verify_attention_mask_workspace(b, R, Hq, Hkv, d, max_prefix)
+    if workspace is None:
+        workspace = attention_workspace(q_blk.device, need)
+    rc = load_library().simsd_verify_attention_mask(
+        _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre) if k_pre.numel() else None,
+        _ptr(v_pre) if v_pre.numel() else None, _ptr(prefix_offsets), _ptr(block_mask), _ptr(out), _ptr(lse),
+        b, R, Hq, Hkv, d, int(max_prefix), float(scale), flags, _ptr(status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("simsd_verify_attention_mask", rc)
     return out
 
 

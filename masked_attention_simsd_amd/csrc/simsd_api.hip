@@ -94,6 +94,7 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
   a.part_ml = reinterpret_cast<float*>(ws + plan.counters_bytes);
   a.part_o = reinterpret_cast<float*>(ws + plan.counters_bytes + plan.ml_bytes);
   a.b = b, a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv, a.d = d;
+  a.nblk = 2 * B;
   a.row0 = rule == SIMSD_DATA_SKIP ? B : 0;
   a.nrows = rule == SIMSD_DATA_SKIP ? B : 2 * B;
   a.M = a.nrows * a.G;
@@ -177,6 +178,77 @@ int simsd_verify_attention_rope(const void* q_blk, const void* k_blk, const void
   return verify_attention_impl(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, b, B, Hq,
                                Hkv, d, max_prefix, scale, flags, status, workspace, ws_bytes, stream,
                                &rope);
+}
+
+size_t simsd_verify_attention_mask_workspace(int b, int R, int Hq, int Hkv, int d, int max_prefix) {
+  if (R < 1 || R > 128 || check_common(b, 1, Hq, Hkv, d) || max_prefix < 0 || max_prefix > simsd::kMaxPrefix)
+    return 0;
+  const simsd::AttnPlan plan = simsd::plan_attention_rows(b, R, Hq, Hkv, d, max_prefix);
+  if (static_cast<long>(b) * Hkv * plan.row_slices > simsd::kAttnMaxUnits) return 0;
+  return plan.total_bytes;
+}
+
+int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
+                                const void* v_pre, const int32_t* prefix_offsets, const uint64_t* block_mask,
+                                void* out, float* lse, int b, int R, int Hq, int Hkv, int d, int max_prefix,
+                                float scale, uint32_t flags, int32_t* status, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  if (!q_blk || !k_blk || !v_blk || !prefix_offsets || !block_mask || !out) return SIMSD_ERR_NULL;
+  if (max_prefix > 0 && (!k_pre || !v_pre)) return SIMSD_ERR_NULL;
+  if (R < 1 || R > 128) return SIMSD_ERR_SIZE;
+  int rc = check_common(b, 1, Hq, Hkv, d);
+  if (rc) return rc;
+  if (max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return SIMSD_ERR_SIZE;
+  if (flags & ~(SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR)) return SIMSD_ERR_FLAGS;
+  if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
+      (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)) ||
+      (reinterpret_cast<uintptr_t>(block_mask) & 7u))
+    return SIMSD_ERR_ALIGN;
+  const simsd::AttnPlan plan = simsd::plan_attention_rows(b, R, Hq, Hkv, d, max_prefix);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || ws_bytes < plan.total_bytes)
+    return SIMSD_ERR_WORKSPACE;
+  simsd::AttnArgs a{};
+  a.q_blk = static_cast<const uint16_t*>(q_blk);
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.k_pre = static_cast<const uint16_t*>(k_pre);
+  a.v_pre = static_cast<const uint16_t*>(v_pre);
+  a.offsets = prefix_offsets;
+  a.tau = nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.status = status;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + plan.counters_bytes);
+  a.part_o = reinterpret_cast<float*>(ws + plan.counters_bytes + plan.ml_bytes);
+  a.b = b, a.B = 0, a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv, a.d = d;
+  a.nblk = R;
+  a.row0 = 0;
+  a.nrows = R;
+  a.M = R * a.G;
+  a.row_slices = plan.row_slices;
+  a.chunk = plan.chunk;
+  a.nsplit = plan.nsplit;
+  a.shift = plan.shift;
+  a.max_prefix = max_prefix;
+  if (static_cast<long>(b) * Hkv * plan.row_slices > simsd::kAttnMaxUnits) return SIMSD_ERR_SIZE;
+  const long total = static_cast<long>(b) * Hkv * plan.row_slices * plan.nsplit;
+  if (total > (1L << 30)) return SIMSD_ERR_SIZE;
+  a.total_real = static_cast<int>(total);
+  a.total_grid = static_cast<int>((total + 7) / 8 * 8);
+  const float sc = scale > 0.0f ? scale : 1.0f / std::sqrt(static_cast<float>(d));
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.data_rule = 0;
+  a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
+  a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  a.xcd_remap = plan.xcd_remap;
+  a.rotate = plan.rotate;
+  a.mask_mode = 1;
+  a.block_mask = block_mask;
+  a.mask_words = (R + 63) / 64;
+  return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
 }
 
 size_t simsd_accept_workspace(int b, int B, int V) {

@@ -86,6 +86,7 @@ struct AttnArgs {
   float* part_ml;     // [unit_slice][split][row] x (m, l)
   int32_t* counters;  // [unit_slice]
   int b, B, Hq, Hkv, G, d;
+  int nblk;           // block rows (and keys) per sequence: 2B, or R with an explicit mask
   int row0, nrows;    // block rows computed: [row0, row0 + nrows)
   int M;              // query rows per (sequence, KV head) = nrows * G
   int row_slices;     // ceil(M / rows per workgroup)
@@ -103,6 +104,11 @@ struct AttnArgs {
   int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
   // RoPE-copy fused into the prologue (rope != 0): query rows and block key
   // rows are rotated on the fly; the rotated block keys go to k_rot if set
+  // explicit block mask (mask_mode): bit c of word c/64 of row r's
+  // mask_words words says whether row r sees block key c; no tau
+  int mask_mode;
+  const uint64_t* block_mask;  // [b][nblk][mask_words]
+  int mask_words;
   int rope;
   const int32_t* start_pos;
   int rope_interleaved, rope_no_copy;
@@ -155,6 +161,8 @@ constexpr long kMaxRopeTableBytes = 64 * 1024;  // fused RoPE cos/sin table (LDS
 constexpr int kAttnMaxUnits = kMaxSeqCounters;  // (sequence, KV head, row slice) units per call
 
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule);
+// the same for `nrows` computed query rows per sequence (explicit-mask calls)
+AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_prefix);
 
 hipError_t launch_rope_copy(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_verify_attention(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);

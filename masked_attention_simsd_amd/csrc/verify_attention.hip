@@ -258,7 +258,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   const int slice = us % a.row_slices;
   const int unit = us / a.row_slices;
   const int s = unit / a.Hkv, g = unit % a.Hkv;
-  const int B = a.B, twoB = 2 * a.B;
+  // block keys: the 2B rows of the paired block, or the R rows of an
+  // explicit-mask call (a.mask_mode: no tau, B = 0)
+  const int B = a.B, twoB = a.nblk;
 
   int P = a.offsets[s + 1] - a.offsets[s];
   const bool bad_prefix = P < 0 || P > a.max_prefix;
@@ -373,6 +375,18 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
       qreg[qb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * a16));
     r_q[qb] = r;
   }
+  // explicit mask: this lane's rows' mask words (<= 128 block keys), requested
+  // with the queries (split 0 only: it takes the block tiles)
+  uint64_t mword[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mword[qb][0] = mword[qb][1] = 0;
+    if (a.mask_mode && split == 0) {
+      const uint64_t* mrow = a.block_mask + (static_cast<size_t>(s) * twoB + r_q[qb]) * a.mask_words;
+      mword[qb][0] = mrow[0];
+      if (a.mask_words > 1) mword[qb][1] = mrow[1];
+    }
+  }
 
   if constexpr (ROPE) {
     // cos/sin of every (block position, frequency) this workgroup needs,
@@ -415,7 +429,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int r = r_q[qb];
     slot_q[qb] = r >= B;
-    tau_q[qb] = tau_s[r >= B ? r - B : r];
+    tau_q[qb] = a.mask_mode ? 0 : tau_s[r >= B ? r - B : r];
     if constexpr (ROPE) rope_rows<D, KK>(qreg[qb], rope_pos_row(r, B, a.rope_no_copy), a16, a.rope_interleaved, rope_tab);
   }
   // Temporal mask of this lane's keys in the block tiles, evaluated once here
@@ -434,8 +448,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int c = bt * TK + kw0 + 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
-            if (c < twoB && block_allowed(slot_q[qb], tau_q[qb], c, B, tau_s, a.data_rule))
-              blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
+            const bool ok = a.mask_mode ? ((mword[qb][c >> 6] >> (c & 63)) & 1ull) != 0
+                                        : block_allowed(slot_q[qb], tau_q[qb], c, B, tau_s, a.data_rule);
+            if (c < twoB && ok) blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
           }
     }
   }
@@ -805,7 +820,8 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     const int r = a.row0 + m / a.G;
     const int h = g * a.G + m % a.G;
     const size_t orow = (static_cast<size_t>(s) * twoB + r) * a.Hq + h;
-    const float inv_l = 1.0f / l_tot[qb];
+    // a row that sees no key at all (explicit mask, empty prefix) gives 0
+    const float inv_l = l_tot[qb] > 0.0f ? 1.0f / l_tot[qb] : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const f32x4 o = oacc[qb][db] * inv_l;
@@ -909,9 +925,12 @@ int env_int(const char* name, int dflt) {
 // resident at once, two per CU), fewer units get ceil(256 / units) splits.
 // Tuning overrides: SIMSD_ATTN_TARGET_WG, SIMSD_ATTN_CHUNK_MAX, SIMSD_ATTN_PIPE.
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule) {
+  return plan_attention_rows(b, data_rule == 2 ? B : 2 * B, Hq, Hkv, d, max_prefix);
+}
+
+AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_prefix) {
   AttnPlan p{};
   const int G = Hq / Hkv;
-  const int nrows = data_rule == 2 ? B : 2 * B;
   const int M = nrows * G;
   if (M <= 16) {
     p.nwc = 1, p.qb = 1;

@@ -55,3 +55,15 @@ def subset_sequences(x: dict, seqs) -> dict:
     idx = torch.tensor(list(seqs))
     return dict(k_pre=kp, v_pre=vp, prefix_offsets=noff, q_blk=x["q_blk"][idx],
                 k_blk=x["k_blk"][idx], v_blk=x["v_blk"][idx], tau=x["tau"][idx])
+
+
+def pack_mask(allowed) -> torch.Tensor:
+    """bool [b][R][R] -> int64 [b][R][ceil(R/64)] bit words (bit c % 64 of
+    word c // 64 of row r set when row r sees block key c)."""
+    a = np.asarray(allowed, dtype=bool)
+    b, R, _ = a.shape
+    W = (R + 63) // 64
+    words = np.zeros((b, R, W), dtype=np.uint64)
+    for c in range(R):
+        words[:, :, c // 64] |= a[:, :, c].astype(np.uint64) << np.uint64(c % 64)
+    return torch.from_numpy(words.view(np.int64))

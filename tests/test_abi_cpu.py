@@ -171,3 +171,22 @@ def test_accept_logits_host_errors(lib):
     n = lib.simsd_accept_logits_workspace(8, 16, 151936)
     assert n > lib.simsd_accept_workspace(8, 16, 151936) and n % 256 == 0
     assert lib.simsd_accept_logits_workspace(65536, 64, 1 << 21) == 0  # statistics units over 2^24
+
+
+def test_attention_mask_host_errors(lib):
+    def f(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, off=FAKE, m=FAKE, out=FAKE, lse=None, b=2, R=24,
+                 Hq=8, Hkv=2, d=128, maxp=100, scale=0.0, flags=0, status=None, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.simsd_verify_attention_mask(a["q"], a["k"], a["v"], a["kp"], a["vp"], a["off"], a["m"], a["out"],
+                                               a["lse"], a["b"], a["R"], a["Hq"], a["Hkv"], a["d"], a["maxp"],
+                                               a["scale"], a["flags"], a["status"], a["ws"], a["wsb"], None)
+    assert f(m=None) == 1
+    assert f(R=0) == 2
+    assert f(R=129) == 2
+    assert f(flags=1) == 5  # data-row rules do not apply
+    assert f(m=ctypes.c_void_p(0x100004)) == 7
+    assert f(Hq=6, Hkv=4) == 3
+    assert f(ws=None) == 6
+    assert f(wsb=lib.simsd_verify_attention_mask_workspace(2, 24, 8, 2, 128, 100) - 1) == 6
+    assert lib.simsd_verify_attention_mask_workspace(2, 129, 8, 2, 128, 100) == 0
