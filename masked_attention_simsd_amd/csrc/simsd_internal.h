@@ -86,7 +86,6 @@ struct AttnArgs {
   float* part_ml;     // [unit_slice][split][row] x (m, l)
   int32_t* counters;  // [unit_slice]
   int b, B, Hq, Hkv, G, d;
-  int nblk;           // block rows (and keys) per sequence: 2B, or R with an explicit mask
   int row0, nrows;    // block rows computed: [row0, row0 + nrows)
   int M;              // query rows per (sequence, KV head) = nrows * G
   int row_slices;     // ceil(M / rows per workgroup)
@@ -104,16 +103,17 @@ struct AttnArgs {
   int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
   // RoPE-copy fused into the prologue (rope != 0): query rows and block key
   // rows are rotated on the fly; the rotated block keys go to k_rot if set
-  // explicit block mask (mask_mode): bit c of word c/64 of row r's
-  // mask_words words says whether row r sees block key c; no tau
-  int mask_mode;
-  const uint64_t* block_mask;  // [b][nblk][mask_words]
-  int mask_words;
   int rope;
   const int32_t* start_pos;
   int rope_interleaved, rope_no_copy;
   uint16_t* k_rot;
   double rope_inv_freq[kMaxRopeFreqs];  // base^(-2i/d), i < d/2
+  // explicit block mask (mask_mode): bit c of word c/64 of row r's
+  // mask_words words says whether row r sees block key c; no tau
+  int mask_mode;
+  int nblk;  // block rows (and keys) per sequence: R (2B without a mask)
+  const uint64_t* block_mask;  // [b][nblk][mask_words]
+  int mask_words;
 };
 
 struct AttnPlan {

@@ -54,6 +54,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define SIMSD_LDS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.6931471805599453f;
+// block-key rule of a kernel instance (its MODE template argument)
+constexpr int kModeTau = 0, kModeTauRope = 1, kModeMask = 2;
 constexpr int TK = kAttnTileKeys;  // chunk granularity of the split plan
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
@@ -215,10 +217,17 @@ __device__ __forceinline__ void rope_rows(bf16x8 (&x)[KK], int pr, int a16, int 
 // independent waves on each SIMD, so one's MFMA work overlaps the other's
 // softmax; their states are merged through LDS at the end); TK keys per staged
 // tile; NS tiles in the LDS ring (NS - 1 in flight while one is consumed).
-// ROPE: RoPE-copy fused into the prologue -- the query rows and the block key
-// rows are rotated on the fly from a per-workgroup cos/sin table (dynamic LDS).
-template <int D, int NW, int NWC, int QB, int TKEYS, int NS, int KS, bool ROPE, bool OUT_F32>
+// MODE selects the block-key rule and is fixed at compile time, so the
+// temporal-mask kernels carry none of the other modes' code:
+//   kModeTau     the temporal mask from tau;
+//   kModeTauRope the same with RoPE-copy fused into the prologue -- the query
+//                rows and the block key rows are rotated on the fly from a
+//                per-workgroup cos/sin table (dynamic LDS);
+//   kModeMask    an explicit block mask (bit words per block row), no tau.
+template <int D, int NW, int NWC, int QB, int TKEYS, int NS, int KS, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
+  constexpr bool ROPE = MODE == kModeTauRope;
+  constexpr bool MASK = MODE == kModeMask;
   constexpr int TK = TKEYS;         // keys per staged tile
   constexpr int KK = D / 32;          // MFMA k-steps of Q.K
   constexpr int DB = D / 16;          // 16-wide d blocks of P.V
@@ -259,8 +268,8 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   const int unit = us / a.row_slices;
   const int s = unit / a.Hkv, g = unit % a.Hkv;
   // block keys: the 2B rows of the paired block, or the R rows of an
-  // explicit-mask call (a.mask_mode: no tau, B = 0)
-  const int B = a.B, twoB = a.nblk;
+  // explicit-mask call (no tau, B = 0)
+  const int B = a.B, twoB = MASK ? a.nblk : 2 * a.B;
 
   int P = a.offsets[s + 1] - a.offsets[s];
   const bool bad_prefix = P < 0 || P > a.max_prefix;
@@ -358,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   const int kh = wave / NWC;   // key slice of every tile (KS = 2)
   const bool owner = computes && kh == 0;  // finishes the rows after the loop
   const int kw0 = kh * TKW;                // first key of this wave's slice of a tile
-  const int tau_ld = (tid < B) ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
+  const int tau_ld = (!MASK && tid < B) ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
   // Lanes past the unit's M rows load (and later compute) a copy of its last
   // row: their results are never stored, and unconditional loads keep the
   // compiler from waiting on them (and so on the DMA ring) right here.
@@ -377,14 +386,16 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   }
   // explicit mask: this lane's rows' mask words (<= 128 block keys), requested
   // with the queries (split 0 only: it takes the block tiles)
-  uint64_t mword[QB][2];
+  // (two arrays, not one of pairs: a pair selected by a runtime condition
+  // would be folded into an indexed access, which moves it to scratch)
+  uint64_t mlo[QB], mhi[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mword[qb][0] = mword[qb][1] = 0;
-    if (a.mask_mode && split == 0) {
+    mlo[qb] = mhi[qb] = 0;
+    if (MASK && split == 0) {
       const uint64_t* mrow = a.block_mask + (static_cast<size_t>(s) * twoB + r_q[qb]) * a.mask_words;
-      mword[qb][0] = mrow[0];
-      if (a.mask_words > 1) mword[qb][1] = mrow[1];
+      mlo[qb] = mrow[0];
+      if (a.mask_words > 1) mhi[qb] = mrow[1];
     }
   }
 
@@ -429,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int r = r_q[qb];
     slot_q[qb] = r >= B;
-    tau_q[qb] = a.mask_mode ? 0 : tau_s[r >= B ? r - B : r];
+    tau_q[qb] = MASK ? 0 : tau_s[r >= B ? r - B : r];
     if constexpr (ROPE) rope_rows<D, KK>(qreg[qb], rope_pos_row(r, B, a.rope_no_copy), a16, a.rope_interleaved, rope_tab);
   }
   // Temporal mask of this lane's keys in the block tiles, evaluated once here
@@ -448,9 +459,12 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int c = bt * TK + kw0 + 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
-            const bool ok = a.mask_mode ? ((mword[qb][c >> 6] >> (c & 63)) & 1ull) != 0
-                                        : block_allowed(slot_q[qb], tau_q[qb], c, B, tau_s, a.data_rule);
-            if (c < twoB && ok) blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
+            bool ok;
+            if constexpr (MASK)
+              ok = c < twoB && (((c >= 64 ? mhi[qb] : mlo[qb]) >> (c & 63)) & 1ull) != 0;
+            else
+              ok = c < twoB && block_allowed(slot_q[qb], tau_q[qb], c, B, tau_s, a.data_rule);
+            if (ok) blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
           }
     }
   }
@@ -820,8 +834,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     const int r = a.row0 + m / a.G;
     const int h = g * a.G + m % a.G;
     const size_t orow = (static_cast<size_t>(s) * twoB + r) * a.Hq + h;
-    // a row that sees no key at all (explicit mask, empty prefix) gives 0
-    const float inv_l = l_tot[qb] > 0.0f ? 1.0f / l_tot[qb] : 0.0f;
+    // a row that sees no key at all (explicit mask, empty prefix) gives 0;
+    // under tau every row sees at least itself or its data partner
+    const float inv_l = (!MASK || l_tot[qb] > 0.0f) ? 1.0f / l_tot[qb] : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const f32x4 o = oacc[qb][db] * inv_l;
@@ -846,28 +861,29 @@ inline size_t rope_table_bytes(const AttnArgs& a) {
   return static_cast<size_t>(npos) * (a.d / 2) * 2 * sizeof(double);
 }
 
-template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1, bool ROPE = false>
+template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1, int MODE = kModeTau>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(a.total_grid)), block(NW * 64);
-  const size_t dyn = ROPE ? rope_table_bytes(a) : 0;
+  const size_t dyn = MODE == kModeTauRope ? rope_table_bytes(a) : 0;
   if (a.out_f32)
-    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, ROPE, true>), grid, block, dyn, stream, a);
+    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, MODE, true>), grid, block, dyn, stream, a);
   else
-    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, ROPE, false>), grid, block, dyn, stream,
+    hipLaunchKernelGGL((verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, MODE, false>), grid, block, dyn, stream,
                        a);
   return hipGetLastError();
 }
 
-// The fused-RoPE path instantiates only the variants the plan picks by default.
-template <int D>
-hipError_t launch_d_rope(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
-  if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2, 4, 1, true>(a, stream);
-  if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2, 4, 1, true>(a, stream);
-  if (p.qb == 2) return launch_variant<D, 4, 2, 64, 2, 4, 1, true>(a, stream);
+// The fused-RoPE and explicit-mask paths instantiate only the variants the
+// plan picks by default.
+template <int D, int MODE>
+hipError_t launch_d_default(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
+  if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2, 4, 1, MODE>(a, stream);
+  if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2, 4, 1, MODE>(a, stream);
+  if (p.qb == 2) return launch_variant<D, 4, 2, 64, 2, 4, 1, MODE>(a, stream);
   if constexpr (D == 128) {
-    if (p.pipe != 1) return launch_variant<D, 4, 1, 32, 4, 4, 1, true>(a, stream);
+    if (p.pipe != 1) return launch_variant<D, 4, 1, 32, 4, 4, 1, MODE>(a, stream);
   }
-  return launch_variant<D, 4, 1, 64, 2, 4, 1, true>(a, stream);
+  return launch_variant<D, 4, 1, 64, 2, 4, 1, MODE>(a, stream);
 }
 
 template <int D>
@@ -979,7 +995,10 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
 }
 
 hipError_t launch_verify_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
-  if (a.rope) return a.d == 64 ? launch_d_rope<64>(a, p, stream) : launch_d_rope<128>(a, p, stream);
+  if (a.rope)
+    return a.d == 64 ? launch_d_default<64, kModeTauRope>(a, p, stream) : launch_d_default<128, kModeTauRope>(a, p, stream);
+  if (a.mask_mode)
+    return a.d == 64 ? launch_d_default<64, kModeMask>(a, p, stream) : launch_d_default<128, kModeMask>(a, p, stream);
   if (a.d == 64) return launch_d<64>(a, p, stream);
   return launch_d<128>(a, p, stream);
 }
