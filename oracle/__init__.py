@@ -29,6 +29,14 @@ Parity status of each function (what pins it, all in ``tests/test_oracle_*``):
   accept_logits           softmax_rows then accept (both pinned), plus the
                           decision margins a differently rounded softmax may
                           cross (ratio_boundary).
+  commit_kv / pack_regions
+                          pure row movement (numpy indexing, no arithmetic):
+                          pinned by closed forms (identity and reversed tau,
+                          L = 0 and L = B), one-token-at-a-time appends, the
+                          untouched rest of the cache, the overflow and bad-tau
+                          cases, and by the context property -- the first
+                          rejected data row attends over the committed cache to
+                          the same result it had in the round that rejected it.
 """
 from __future__ import annotations
 
@@ -44,6 +52,8 @@ SRC = os.path.join(HERE, "simsd_oracle.c")
 LIB = os.path.join(HERE, "libsimsd_oracle.so")
 
 DATA_CAUSAL, DATA_BIDIR, DATA_SKIP = 0, 1, 2
+# per-sequence status bits of commit_kv
+BAD_TAU, COMMIT_OVERFLOW = 1, 64
 
 _lib = None
 
@@ -280,3 +290,70 @@ def attention_masked(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, allowed,
     _load().simsd_oracle_attention_masked(_p(q), _p(kb), _p(vb), _p(kp), _p(vp), _p(off), _p(al), b, R,
                                           Hq, Hkv, d, float(scale), _p(out), _p(lse))
     return out, lse
+
+
+def pack_regions(cache, offsets, lens, head_major: bool = False):
+    """The packed prefix (cumulative-offset layout) of a cache that gives every
+    sequence a region of rows [offsets[s], offsets[s+1]) of which the first
+    lens[s] are in use. cache is [C][Hkv][d] (or [Hkv][C][d] with head_major).
+    Returns (packed [sum lens][Hkv][d] or [Hkv][sum lens][d], packed_offsets)."""
+    c = np.asarray(cache)
+    off = _i32(offsets)
+    ln = _i32(lens)
+    b = ln.shape[0]
+    rows = [np.arange(off[s], off[s] + ln[s]) for s in range(b)]
+    idx = np.concatenate(rows) if b else np.zeros(0, dtype=np.int64)
+    packed = c[:, idx] if head_major else c[idx]
+    po = np.zeros(b + 1, dtype=np.int32)
+    po[1:] = np.cumsum(ln)
+    return packed, po
+
+
+def commit_kv(k_blk, v_blk, tau, accept_len, k_cache, v_cache, cache_offsets, cache_lens,
+              head_major: bool = False):
+    """Commit the accepted drafts of one verification round to the KV cache
+    ([nl]/[fr] Methodologie 4, Acceptance / Acceptation: the longest prefix
+    accepted along the temporal order is committed and the round repeats).
+
+    Sequence s accepted its first L = accept_len[s] drafts in temporal order:
+    the data tokens D_k with tau(k) <= L. Their key and value rows (block rows
+    k - 1 < B of k_blk / v_blk [b][2B][Hkv][d], already rotated at their own
+    positions) are written, in temporal order t = 1..L (k = tau^-1(t)), to rows
+    cache_lens[s] + t - 1 of the sequence's region [cache_offsets[s],
+    cache_offsets[s+1]) of k_cache / v_cache ([C][Hkv][d], or [Hkv][C][d] with
+    head_major), and the sequence's used length becomes cache_lens[s] + L.
+    Nothing of sequence s is written, and its length is kept, when tau[s] is not
+    a permutation (status BAD_TAU) or when L is outside 0..B, the length is
+    negative, or the region cannot hold L more rows (COMMIT_OVERFLOW).
+
+    Returns (k_cache', v_cache', lens', status[b]) as new arrays.
+    """
+    kb, vb = np.asarray(k_blk), np.asarray(v_blk)
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    off = _i32(cache_offsets)
+    ln = _i32(cache_lens).copy()
+    t = _i32(tau)
+    L_all = _i32(accept_len)
+    b, B = t.shape
+    status = np.zeros(b, dtype=np.int32)
+    for s in range(b):
+        inv, ok = tau_inverse(t[s])
+        if not ok:
+            status[s] |= BAD_TAU
+            continue
+        L = int(L_all[s])
+        cap = int(off[s + 1]) - int(off[s])
+        if L < 0 or L > B or ln[s] < 0 or int(ln[s]) + L > cap:
+            status[s] |= COMMIT_OVERFLOW
+            continue
+        for step in range(L):
+            k = int(inv[step])  # 0-based position of the draft with label step + 1
+            row = int(off[s]) + int(ln[s]) + step
+            if head_major:
+                kc[:, row] = kb[s, k]
+                vc[:, row] = vb[s, k]
+            else:
+                kc[row] = kb[s, k]
+                vc[row] = vb[s, k]
+        ln[s] += L
+    return kc, vc, ln, status
