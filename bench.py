@@ -337,6 +337,29 @@ def main():
     acc_us = alone(lib.simsd_accept, 2) * 1e6
     acc_logits_us = alone(lib.simsd_accept_logits, 4) * 1e6
     rope_us = alone(lib.simsd_rope_copy, 0) * 1e6
+    # KV commit of set 0's accepted drafts, appended call after call to a
+    # head-major cache whose regions have room for every call (two launches:
+    # the row copies, then the length update)
+    n_commit = min(args.steps, 200)
+    cap = (n_commit + 1) * B
+    kc = torch.empty(Hkv, b * cap, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    ext = torch.cat([torch.arange(b + 1, dtype=torch.int32, device=dev) * cap,
+                     torch.zeros(b, dtype=torch.int32, device=dev)])
+    commit = (P(base["k_blk"]), P(base["v_blk"]), P(base["tau"]), P(Ls[0]), P(kc), P(vc), P(ext),
+              P(ext[b + 1:]), b, B, Hkv, d, binding.SIMSD_KV_HEAD_MAJOR, None, hs)
+    step(0)  # Ls[0]: the accepted lengths of set 0
+    rows = int(Ls[0].sum().item())
+    c0, c1 = ev(), ev()
+    c0.record(stream)
+    for _ in range(n_commit):
+        if lib.simsd_commit_kv(*commit):
+            raise RuntimeError("simsd_commit_kv failed")
+    c1.record(stream)
+    torch.cuda.synchronize()
+    if int(ext[b + 1:].sum().item()) != rows * n_commit:
+        raise RuntimeError("commit timing: lengths did not advance as expected")
+    commit_us = c0.elapsed_time(c1) / n_commit * 1e3
     # spread of single steps: an event pair around each step
     pairs = [(ev(), ev()) for _ in range(min(args.steps, 200))]
     for i, (e0, e1) in enumerate(pairs):
@@ -380,7 +403,9 @@ def main():
                        "fused_rope": {"verify_attention_rope": round(fused_us, 3),
                                       "step": round(fused_step_ms * 1e3, 3)},
                        "accept_logits": {"us": round(acc_logits_us, 3),
-                                         "logits_GBps": round(2 * b * B * w.V * 4 / acc_logits_us / 1e3, 1)}},
+                                         "logits_GBps": round(2 * b * B * w.V * 4 / acc_logits_us / 1e3, 1)},
+                       "commit_kv": {"us": round(commit_us, 3), "rows_committed": rows,
+                                     "bytes_moved": rows * Hkv * d * 2 * 2 * 2}},
         "attention_mfma": {"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
                            "ceiling_at_hbm_peak": round(min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS), 4),
                            "flops_per_launch": flops},

@@ -71,6 +71,8 @@ typedef enum {
 #define SIMSD_DEV_SYNC_TIMEOUT 32 /* acceptance: a segment mass of this sequence was not seen within
                                      the poll bound; the correction is unspecified and the workspace
                                      must be zeroed again before reuse (not expected to occur) */
+#define SIMSD_DEV_COMMIT_OVERFLOW 64 /* KV commit: accept_len outside 0..B, a negative used length, or
+                                        a cache region too small; nothing of the sequence written */
 
 /* simsd_rope_copy flags */
 #define SIMSD_ROPE_HALF 0u        /* rotate-half pairing (i, i + d/2) (default) */
@@ -83,6 +85,8 @@ typedef enum {
 #define SIMSD_DATA_SKIP 2u   /* data rows are not computed; their out/lse rows are untouched */
 #define SIMSD_OUT_F32 4u     /* out is fp32 instead of bf16 */
 #define SIMSD_KV_HEAD_MAJOR 8u /* k_pre / v_pre are [Hkv][sum P][d] instead of [sum P][Hkv][d] */
+#define SIMSD_PREFIX_LENS 16u  /* prefix_offsets holds 2b+1 int32: b+1 region bounds, then b used
+                                  lengths (a cache with room to grow; see simsd_commit_kv) */
 
 /*
  * simsd_rope_copy -- rotary position embedding of the block's queries and
@@ -130,7 +134,14 @@ int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, i
  *                        lets each KV head's keys stream contiguously (faster
  *                        on long prefixes); sum_s P_s is read from
  *                        prefix_offsets[b].
- *   prefix_offsets       int32 [b+1], non-decreasing, offsets[0] = 0
+ *   prefix_offsets       int32 [b+1], non-decreasing, offsets[0] = 0. With
+ *                        SIMSD_PREFIX_LENS it holds 2b+1 values: the b+1
+ *                        bounds of each sequence's cache region, followed by
+ *                        the b used lengths P_s; the prefix of sequence s is
+ *                        then the first P_s rows of its region (rows
+ *                        offsets[s] .. offsets[s] + P_s - 1; the head-major
+ *                        stride is offsets[b]), and P_s larger than the region
+ *                        is clamped to it and flagged SIMSD_DEV_BAD_PREFIX.
  *   tau                  int32 [b][B]
  *   out                  [b][2B][Hq][d], bf16 (or fp32 with SIMSD_OUT_F32)
  *   lse                  optional fp32 [b][2B][Hq]: natural-log sum of exp of
@@ -179,7 +190,7 @@ size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, in
  *   q_blk, k_blk, v_blk  bf16 [b][R][Hq|Hkv|Hkv][d], R block rows (1..128)
  *   block_mask   uint64 [b][R][ceil(R/64)], 8-byte aligned: bit (c % 64) of
  *                word c / 64 of row r set = row r sees block key c
- *   flags        SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR only
+ *   flags        SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS only
  *   status       optional int32 [b]; SIMSD_DEV_BAD_PREFIX
  *   other arguments as for simsd_verify_attention; the workspace size comes
  *   from simsd_verify_attention_mask_workspace.
@@ -305,6 +316,51 @@ int simsd_accept_logits(const float* target_logits, const float* draft_logits, f
 
 /* Workspace bytes simsd_accept_logits needs (0 on bad sizes). */
 size_t simsd_accept_logits_workspace(int b, int B, int V);
+
+/*
+ * simsd_commit_kv -- commit the accepted drafts of a verification round to the
+ * KV cache, so that the next round verifies against them ([nl]/[fr]
+ * Methodologie 4, Acceptance / Acceptation: the longest prefix accepted along
+ * the temporal order is committed and the round repeats; compatibility with a
+ * KV cache, [nl] Belangrijkste Bijdragen 3 / [fr] Principales Contributions).
+ *
+ * Sequence s accepted its first L = accept_len[s] drafts in temporal order,
+ * the data tokens D_k with tau(k) <= L. Their key and value rows (block rows
+ * k - 1 of k_blk / v_blk, already rotated at their own positions) are written
+ * in temporal order t = 1..L (k = tau^-1(t)) to rows cache_lens[s] + t - 1 of
+ * the sequence's cache region, and cache_lens[s] grows by L. Under the
+ * default data-row rule (SIMSD_DATA_CAUSAL) each of these rows was computed
+ * from exactly the context a token-by-token decode in temporal order gives it.
+ *
+ *   k_blk, v_blk     bf16 [b][2B][Hkv][d] (rows 0..B-1 are D_1..D_B)
+ *   tau              int32 [b][B]
+ *   accept_len       int32 [b] (the output of simsd_accept)
+ *   k_cache, v_cache bf16 cache, token-major [C][Hkv][d] or, with
+ *                    SIMSD_KV_HEAD_MAJOR, head-major [Hkv][C][d], C =
+ *                    cache_offsets[b]; sequence s owns rows cache_offsets[s]
+ *                    .. cache_offsets[s+1]-1, of which the first
+ *                    cache_lens[s] are in use. Only the appended rows are
+ *                    written.
+ *   cache_offsets    int32 [b+1], non-decreasing, region bounds
+ *   cache_lens       int32 [b], updated in place (written by a second launch
+ *                    on the same stream, after every row has been copied).
+ *                    Laid out right after the region bounds (cache_lens =
+ *                    cache_offsets + b + 1), the same array serves as the
+ *                    prefix_offsets of simsd_verify_attention with
+ *                    SIMSD_PREFIX_LENS and as the start_pos of the next round.
+ *   flags            SIMSD_KV_HEAD_MAJOR or 0
+ *   status           optional int32 [b]; SIMSD_DEV_BAD_TAU or
+ *                    SIMSD_DEV_COMMIT_OVERFLOW (L outside 0..B, a negative
+ *                    length, or L more rows do not fit the region): nothing of
+ *                    that sequence is written and its length is kept.
+ * The cache must not overlap k_blk / v_blk, and cache_lens must not overlap
+ * tau or accept_len.
+ * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, Hkv<1), _HEAD_DIM,
+ * _FLAGS, _ALIGN (bf16 tensors 16-byte aligned), _LAUNCH.
+ */
+int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, const int32_t* accept_len,
+                    void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens, int b,
+                    int B, int Hkv, int d, uint32_t flags, int32_t* status, void* stream);
 
 /* Static text for a simsd_status_t value. */
 const char* simsd_status_string(int code);

@@ -21,16 +21,17 @@ LIB_PATH = os.path.join(PKG, "libsimsd.so")
 # flag and status values, as in include/simsd.h
 SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY = 0, 1, 2
 SIMSD_DATA_CAUSAL, SIMSD_DATA_BIDIR, SIMSD_DATA_SKIP, SIMSD_OUT_F32 = 0, 1, 2, 4
-SIMSD_KV_HEAD_MAJOR = 8
+SIMSD_KV_HEAD_MAJOR, SIMSD_PREFIX_LENS = 8, 16
 SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
 SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
+SIMSD_DEV_COMMIT_OVERFLOW = 64
 
 EXPORTS = (
     "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_rope",
     "simsd_verify_attention_workspace", "simsd_verify_attention_mask",
     "simsd_verify_attention_mask_workspace",
     "simsd_accept", "simsd_accept_workspace", "simsd_accept_logits", "simsd_accept_logits_workspace",
-    "simsd_status_string", "simsd_last_hip_error",
+    "simsd_commit_kv", "simsd_status_string", "simsd_last_hip_error",
 )
 
 
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_accept_workspace.restype = Z
         lib.simsd_accept_logits.argtypes = [P, P, F, P, P, P, I, I, I, P, P, P, P, Z, P]
         lib.simsd_accept_logits.restype = I
+        lib.simsd_commit_kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, U, P, P]
+        lib.simsd_commit_kv.restype = I
         lib.simsd_accept_logits_workspace.argtypes = [I, I, I]
         lib.simsd_accept_logits_workspace.restype = Z
         lib.simsd_status_string.argtypes = [I]
@@ -113,6 +116,17 @@ def _need(t, name, dtype, dims=None, device=True):
         raise ValueError(f"{name} must be contiguous")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+
+
+def _offsets_len(b: int, flags: int) -> int:
+    """prefix_offsets holds b+1 bounds, followed by b used lengths with SIMSD_PREFIX_LENS."""
+    return 2 * b + 1 if flags & SIMSD_PREFIX_LENS else b + 1
+
+
+def _max_prefix(prefix_offsets, b: int) -> int:
+    """The largest region (a bound on every prefix length; a device-to-host copy)."""
+    off = prefix_offsets[:b + 1].cpu()
+    return int((off[1:] - off[:-1]).max()) if b > 0 else 0
 
 
 def simsd_rope_copy(q_blk, k_blk, start_pos, rope_base: float = 10000.0, flags: int = 0,
@@ -215,11 +229,10 @@ def _attention(fn, q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, 
     pre_ok = (k_pre.shape[0] == Hkv and k_pre.shape[2] == d) if head_major else k_pre.shape[1:] == (Hkv, d)
     if (twoB % 2 or tuple(k_blk.shape) != (b, twoB, Hkv, d) or tuple(v_blk.shape) != (b, twoB, Hkv, d)
             or not pre_ok or v_pre.shape != k_pre.shape
-            or prefix_offsets.shape[0] != b + 1 or tuple(tau.shape) != (b, B)):
+            or prefix_offsets.shape[0] != _offsets_len(b, flags) or tuple(tau.shape) != (b, B)):
         raise ValueError("inconsistent shapes")
     if max_prefix is None:
-        off = prefix_offsets.cpu()
-        max_prefix = int((off[1:] - off[:-1]).max()) if b > 0 else 0
+        max_prefix = _max_prefix(prefix_offsets, b)
     out_f32 = bool(flags & SIMSD_OUT_F32)
     if out is None:
         out = torch.empty_like(q_blk, dtype=torch.float32 if out_f32 else torch.bfloat16)
@@ -268,12 +281,11 @@ def simsd_verify_attention_mask(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offset
     head_major = bool(flags & SIMSD_KV_HEAD_MAJOR)
     pre_ok = (k_pre.shape[0] == Hkv and k_pre.shape[2] == d) if head_major else k_pre.shape[1:] == (Hkv, d)
     if (tuple(k_blk.shape) != (b, R, Hkv, d) or tuple(v_blk.shape) != (b, R, Hkv, d) or not pre_ok
-            or v_pre.shape != k_pre.shape or prefix_offsets.shape[0] != b + 1
+            or v_pre.shape != k_pre.shape or prefix_offsets.shape[0] != _offsets_len(b, flags)
             or tuple(block_mask.shape) != (b, R, (R + 63) // 64)):
         raise ValueError("inconsistent shapes")
     if max_prefix is None:
-        off = prefix_offsets.cpu()
-        max_prefix = int((off[1:] - off[:-1]).max()) if b > 0 else 0
+        max_prefix = _max_prefix(prefix_offsets, b)
     out_f32 = bool(flags & SIMSD_OUT_F32)
     if out is None:
         out = torch.empty_like(q_blk, dtype=torch.float32 if out_f32 else torch.bfloat16)
@@ -359,3 +371,43 @@ def simsd_accept_logits(target_logits, draft_logits, draft_tokens, tau, uniforms
                                             _stream(stream))
     _check("simsd_accept_logits", rc)
     return accept_len, correction_token
+
+
+def cache_offsets_with_lens(offsets, lens):
+    """One int32 device array [2b+1]: region bounds then used lengths. Pass it
+    as prefix_offsets with SIMSD_PREFIX_LENS; its tail view ([b+1:]) is the
+    cache_lens of simsd_commit_kv and the start_pos of the next round."""
+    return torch.cat([offsets.to(torch.int32), lens.to(torch.int32)]).contiguous()
+
+
+def simsd_commit_kv(k_blk, v_blk, tau, accept_len, k_cache, v_cache, cache_offsets, cache_lens,
+                    flags: int = 0, status=None, stream=None):
+    """Append each sequence's accepted drafts (tau(k) <= accept_len[s]) to its
+    cache region, in temporal order, and advance cache_lens in place.
+
+    k_blk / v_blk [b][2B][Hkv][d] bf16; k_cache / v_cache [C][Hkv][d] (or
+    [Hkv][C][d] with SIMSD_KV_HEAD_MAJOR) bf16; cache_offsets int32 [b+1];
+    cache_lens int32 [b] (may be a view into the array built by
+    cache_offsets_with_lens)."""
+    for t, n in ((k_blk, "k_blk"), (v_blk, "v_blk")):
+        _need(t, n, torch.bfloat16, 4)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, torch.bfloat16, 3)
+    _need(tau, "tau", torch.int32, 2)
+    _need(accept_len, "accept_len", torch.int32, 1)
+    _need(cache_offsets, "cache_offsets", torch.int32, 1)
+    _need(cache_lens, "cache_lens", torch.int32, 1)
+    b, twoB, Hkv, d = k_blk.shape
+    B = twoB // 2
+    head_major = bool(flags & SIMSD_KV_HEAD_MAJOR)
+    cache_ok = (k_cache.shape[0] == Hkv and k_cache.shape[2] == d) if head_major else k_cache.shape[1:] == (Hkv, d)
+    if (twoB % 2 or tuple(v_blk.shape) != tuple(k_blk.shape) or not cache_ok or v_cache.shape != k_cache.shape
+            or tuple(tau.shape) != (b, B) or accept_len.shape[0] != b or cache_offsets.shape[0] < b + 1
+            or cache_lens.shape[0] != b):
+        raise ValueError("inconsistent shapes")
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    rc = load_library().simsd_commit_kv(_ptr(k_blk), _ptr(v_blk), _ptr(tau), _ptr(accept_len), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(cache_offsets), _ptr(cache_lens), b, B, Hkv, d,
+                                        flags, _ptr(status), _stream(stream))
+    _check("simsd_commit_kv", rc)

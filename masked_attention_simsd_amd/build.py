@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsimsd.so")
-SOURCES = ["simsd_api.hip", "rope_copy.hip", "verify_attention.hip", "accept.hip"]
+SOURCES = ["simsd_api.hip", "rope_copy.hip", "verify_attention.hip", "accept.hip", "commit_kv.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -55,7 +55,8 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
   if (rc) return rc;
   if (max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return SIMSD_ERR_SIZE;
   const uint32_t rule = flags & 3u;
-  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR))) return SIMSD_ERR_FLAGS;
+  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS)))
+    return SIMSD_ERR_FLAGS;
   if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)))
@@ -113,6 +114,9 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
   a.data_rule = static_cast<int>(rule);
   a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
   a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  const bool lens = (flags & SIMSD_PREFIX_LENS) != 0;
+  a.prefix_lens = lens ? prefix_offsets + b + 1 : prefix_offsets + 1;
+  a.prefix_lens_are_ends = lens ? 0 : 1;
   a.xcd_remap = plan.xcd_remap;
   a.rotate = plan.rotate;
   if (rope) {
@@ -199,7 +203,7 @@ int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void
   int rc = check_common(b, 1, Hq, Hkv, d);
   if (rc) return rc;
   if (max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return SIMSD_ERR_SIZE;
-  if (flags & ~(SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR)) return SIMSD_ERR_FLAGS;
+  if (flags & ~(SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS)) return SIMSD_ERR_FLAGS;
   if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)) ||
@@ -243,6 +247,9 @@ int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void
   a.data_rule = 0;
   a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
   a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  const bool lens = (flags & SIMSD_PREFIX_LENS) != 0;
+  a.prefix_lens = lens ? prefix_offsets + b + 1 : prefix_offsets + 1;
+  a.prefix_lens_are_ends = lens ? 0 : 1;
   a.xcd_remap = plan.xcd_remap;
   a.rotate = plan.rotate;
   a.mask_mode = 1;
@@ -326,6 +333,40 @@ int simsd_accept_logits(const float* target_logits, const float* draft_logits, f
   a.nseg1 = nseg1;
   a.inv_t = 1.0 / static_cast<double>(temperature);
   return launch_status(simsd::launch_accept_logits(a, static_cast<hipStream_t>(stream)));
+}
+
+int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, const int32_t* accept_len,
+                    void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens, int b,
+                    int B, int Hkv, int d, uint32_t flags, int32_t* status, void* stream) {
+  if (!k_blk || !v_blk || !tau || !accept_len || !k_cache || !v_cache || !cache_offsets || !cache_lens)
+    return SIMSD_ERR_NULL;
+  int rc = check_common(b, B, Hkv, Hkv, d);
+  if (rc) return rc;
+  if (flags & ~SIMSD_KV_HEAD_MAJOR) return SIMSD_ERR_FLAGS;
+  if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
+    return SIMSD_ERR_ALIGN;
+  // the lengths are read by every copy and then rewritten: they must not be
+  // one of the other inputs (the cache and the block are the caller's to keep apart)
+  auto overlap = [](const void* x, size_t nx, const void* y, size_t ny) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
+    return a0 < b0 + ny && b0 < a0 + nx;
+  };
+  const size_t nl = static_cast<size_t>(b) * 4;
+  if (overlap(cache_lens, nl, tau, nl * B) || overlap(cache_lens, nl, accept_len, nl))
+    return SIMSD_ERR_ALIAS;
+  simsd::CommitArgs a{};
+  a.k_blk = static_cast<const uint16_t*>(k_blk);
+  a.v_blk = static_cast<const uint16_t*>(v_blk);
+  a.tau = tau;
+  a.accept_len = accept_len;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.offsets = cache_offsets;
+  a.lens = cache_lens;
+  a.status = status;
+  a.b = b, a.B = B, a.Hkv = Hkv, a.d = d;
+  a.head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  return launch_status(simsd::launch_commit_kv(a, static_cast<hipStream_t>(stream)));
 }
 
 const char* simsd_status_string(int code) {

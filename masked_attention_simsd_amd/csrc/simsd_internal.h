@@ -18,6 +18,7 @@ constexpr int kDevQZero = 4;
 constexpr int kDevBadToken = 8;
 constexpr int kDevBadPrefix = 16;
 constexpr int kDevSyncTimeout = 32;
+constexpr int kDevCommitOverflow = 64;
 
 // bf16 <-> fp32. bf16 is the upper half of an IEEE binary32.
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -114,6 +115,25 @@ struct AttnArgs {
   int nblk;  // block rows (and keys) per sequence: R (2B without a mask)
   const uint64_t* block_mask;  // [b][nblk][mask_words]
   int mask_words;
+  // rows in use of each region [offsets[s], offsets[s+1]): prefix_lens[s], or,
+  // with prefix_lens_are_ends (prefix_lens = offsets + 1, a packed cache),
+  // prefix_lens[s] - offsets[s]
+  const int32_t* prefix_lens;
+  int prefix_lens_are_ends;
+};
+
+struct CommitArgs {
+  const uint16_t* k_blk;  // [b][2B][Hkv][d]
+  const uint16_t* v_blk;
+  const int32_t* tau;         // [b][B]
+  const int32_t* accept_len;  // [b]
+  uint16_t* k_cache;          // [C][Hkv][d] or [Hkv][C][d], C = offsets[b]
+  uint16_t* v_cache;
+  const int32_t* offsets;  // [b+1] region bounds
+  int32_t* lens;           // [b] used rows, updated in place
+  int32_t* status;
+  int b, B, Hkv, d;
+  int head_major;
 };
 
 struct AttnPlan {
@@ -167,6 +187,7 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
 hipError_t launch_rope_copy(const RopeArgs& a, hipStream_t stream);
 hipError_t launch_verify_attention(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+hipError_t launch_commit_kv(const CommitArgs& a, hipStream_t stream);
 // acceptance from logits: the row-statistics pass, then the acceptance kernel
 // in logits mode (same stream)
 hipError_t launch_accept_logits(const AcceptArgs& a, hipStream_t stream);

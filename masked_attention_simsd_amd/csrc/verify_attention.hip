@@ -271,9 +271,16 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   // explicit-mask call (no tau, B = 0)
   const int B = a.B, twoB = MASK ? a.nblk : 2 * a.B;
 
-  int P = a.offsets[s + 1] - a.offsets[s];
-  const bool bad_prefix = P < 0 || P > a.max_prefix;
-  P = P < 0 ? 0 : (P > a.max_prefix ? a.max_prefix : P);
+  // the prefix: the first P rows of the region [offsets[s], offsets[s+1]):
+  // P = prefix_ends[s] - offsets[s] with prefix_ends = offsets + 1 (the whole
+  // region), or P = prefix_lens[s] for a cache with room to grow. Three
+  // independent scalar loads either way, no branch before the first DMA.
+  const int o0 = a.offsets[s];
+  const int cap = a.offsets[s + 1] - o0;
+  int P = a.prefix_lens[s] - (a.prefix_lens_are_ends ? o0 : 0);
+  const int lim = min(a.max_prefix, max(cap, 0));
+  const bool bad_prefix = P < 0 || P > lim;
+  P = P < 0 ? 0 : (P > lim ? lim : P);
   const int ns = P > 0 ? (P + a.chunk - 1) / a.chunk : 1;
   if (split >= ns) return;
   // split 0 also takes the block tiles, so its prefix run is `shift` keys

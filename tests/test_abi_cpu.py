@@ -64,7 +64,7 @@ def test_attention_host_errors(lib):
     assert _attn(lib, Hq=6, Hkv=4) == 3
     assert _attn(lib, d=96) == 4
     assert _attn(lib, flags=3) == 5
-    assert _attn(lib, flags=16) == 5
+    assert _attn(lib, flags=32) == 5
     assert _attn(lib, scale=float("nan")) == 9
     assert _attn(lib, out=MISALIGNED) == 7
     assert _attn(lib, ws=None) == 6
@@ -190,3 +190,27 @@ def test_attention_mask_host_errors(lib):
     assert f(ws=None) == 6
     assert f(wsb=lib.simsd_verify_attention_mask_workspace(2, 24, 8, 2, 128, 100) - 1) == 6
     assert lib.simsd_verify_attention_mask_workspace(2, 129, 8, 2, 128, 100) == 0
+
+
+def test_commit_kv_host_errors(lib):
+    def f(**kw):
+        a = dict(k=FAKE, v=FAKE, tau=ctypes.c_void_p(0x200000), L=ctypes.c_void_p(0x300000), kc=FAKE, vc=FAKE,
+                 off=ctypes.c_void_p(0x400000), lens=ctypes.c_void_p(0x400040), b=4, B=8, Hkv=2, d=128,
+                 flags=0, status=None)
+        a.update(kw)
+        return lib.simsd_commit_kv(a["k"], a["v"], a["tau"], a["L"], a["kc"], a["vc"], a["off"], a["lens"],
+                                   a["b"], a["B"], a["Hkv"], a["d"], a["flags"], a["status"], None)
+    for name in ("k", "v", "tau", "L", "kc", "vc", "off", "lens"):
+        assert f(**{name: None}) == 1, name
+    assert f(b=0) == 2
+    assert f(B=0) == 2
+    assert f(B=65) == 2
+    assert f(Hkv=0) == 2
+    assert f(d=96) == 4
+    assert f(flags=1) == 5
+    assert f(flags=16) == 5
+    assert f(kc=MISALIGNED) == 7
+    assert f(k=MISALIGNED) == 7
+    # the lengths may not be tau or accept_len (they are rewritten after every copy read them)
+    assert f(lens=ctypes.c_void_p(0x200010)) == 10
+    assert f(lens=ctypes.c_void_p(0x300000)) == 10
