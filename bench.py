@@ -68,10 +68,10 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary of `workload`, if it was taken on the current kernel source; else
-    None."""
+def counter_summary(workload, key):
+    """A value from the committed rocprofv3 counter summary of `workload`
+    (HBM bytes per attention launch, MFMA busy fraction), if the summary was
+    taken on the current kernel source; else None."""
     path = counter_file(workload)
     if not os.path.exists(path):
         return None
@@ -83,7 +83,7 @@ def counter_traffic(workload):
     if kv.get("source_sha256_16") != attn_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -373,8 +373,11 @@ def main():
     nbytes, flops = attn_bytes_flops(w, lens, fused=False)
     achieved = nbytes / attn_avg_s / 1e9
     tflops = flops / attn_avg_s / 1e12
-    traffic = counter_traffic(workload)
+    traffic = counter_summary(workload, "hbm_bytes_per_launch")
+    mfma_busy = counter_summary(workload, "mfma_busy_fraction")
     ai = flops / nbytes
+    # the useful-FLOP ceiling if the kernel ran at the HBM peak: min(1, AI / ridge point)
+    ceiling = min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS)
     result = {
         "metric": METRIC,
         "value": round(blocks_per_s, 1),
@@ -407,7 +410,9 @@ def main():
                        "commit_kv": {"us": round(commit_us, 3), "rows_committed": rows,
                                      "bytes_moved": rows * Hkv * d * 2 * 2 * 2}},
         "attention_mfma": {"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
-                           "ceiling_at_hbm_peak": round(min(1.0, ai * HBM_PEAK_GBS / 1e3 / BF16_PEAK_TFLOPS), 4),
+                           "ceiling_at_hbm_peak": round(ceiling, 4),
+                           "frac_of_ceiling": round(tflops / BF16_PEAK_TFLOPS / ceiling, 4),
+                           "counter_mfma_busy": mfma_busy,
                            "flops_per_launch": flops},
         "cpu_baseline": cpu,
     }
