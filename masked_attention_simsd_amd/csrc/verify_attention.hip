@@ -881,12 +881,18 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
 }
 
 // The fused-RoPE and explicit-mask paths instantiate only the variants the
-// plan picks by default.
+// plan picks by default (the same ones as the tau path, so the three agree bit
+// for bit where their rules coincide).
 template <int D, int MODE>
 hipError_t launch_d_default(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2, 4, 1, MODE>(a, stream);
   if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2, 4, 1, MODE>(a, stream);
-  if (p.qb == 2) return launch_variant<D, 4, 2, 64, 2, 4, 1, MODE>(a, stream);
+  if (p.qb == 2) {
+    if constexpr (D == 128) {
+      if (p.pipe == 7) return launch_variant<D, 4, 2, 64, 2, 8, 2, MODE>(a, stream);
+    }
+    return launch_variant<D, 4, 2, 64, 2, 4, 1, MODE>(a, stream);
+  }
   if constexpr (D == 128) {
     if (p.pipe != 1) return launch_variant<D, 4, 1, 32, 4, 4, 1, MODE>(a, stream);
   }
@@ -982,13 +988,20 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
   chunk = std::max(TK, std::min(chunk, chunk_max));
   nsplit = std::max(1, (max_prefix + chunk - 1) / chunk);
   // Key-tile ring (keys per tile x stages), for d = 128. 64 rows: 0 = 32x4,
-  // 1 = 64x2, 2 = 64x3, 3 = 32x3, 4 = 32x6, 5 = 32x8, 6 = 64x4. 128 rows:
-  // 0 = 4 waves x 2 row blocks 64x2, 1 = 4x2 32x4, 2 = 4x2 64x3, 3 = 8 waves
-  // x 1 32x4, 4 = 8x1 64x2, 5 = 8x1 32x6, 6 = 8x1 64x3. With one workgroup per
-  // CU the deeper 32x4 ring keeps more bytes in flight; with two per CU the
-  // other workgroup covers the latency and 64-key tiles halve the barriers.
+  // 1 = 64x2, 2 = 64x3, 3 = 32x3, 4 = 32x6, 5 = 32x8, 6 = 64x4, 7-9 = 64x2,
+  // 64x3, 64x4 with two waves per row group. 128 rows: 0 = 4 waves x 2 row
+  // blocks 64x2, 1 = 4x2 32x4, 2 = 4x2 64x3, 3 = 8 waves x 1 32x4, 4 = 8x1
+  // 64x2, 5 = 8x1 32x6, 6 = 8x1 64x3, 7 = 4x2 64x2 with two waves per row
+  // group, 8 = the same 64x3. With one 64-row workgroup per CU the deeper 32x4
+  // ring keeps more bytes in flight; with two per CU the other workgroup covers
+  // the latency and 64-key tiles halve the barriers. A 128-row workgroup
+  // carries twice the MFMA and softmax work per byte; alone on its CU it runs
+  // best with two waves per row group on every SIMD, each taking half of every
+  // key tile, so one wave's MFMA work overlaps the other's softmax (b16: 116
+  // vs 119 us, measured interleaved on two boxes).
   const long wgs = units * nsplit;
-  p.pipe = env_int("SIMSD_ATTN_PIPE", (p.qb == 1 && wgs > 256) ? 1 : 0);
+  const int pipe_default = p.qb == 1 ? (wgs > 256 ? 1 : 0) : (wgs <= 256 ? 7 : 0);
+  p.pipe = env_int("SIMSD_ATTN_PIPE", pipe_default);
   p.chunk = chunk;
   p.nsplit = nsplit;
   // tuning: prefix keys moved off split 0, which also takes the block tiles
