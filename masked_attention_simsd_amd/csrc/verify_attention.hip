@@ -883,13 +883,32 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
 // The fused-RoPE and explicit-mask paths instantiate only the variants the
 // plan picks by default (the same ones as the tau path, so the three agree bit
 // for bit where their rules coincide).
+// LDS a workgroup may use on gfx950 (static and dynamic together).
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+
+// Whether an instance's static LDS plus `dyn` bytes of dynamic LDS fit a workgroup.
+template <int D, int NWC, int QB, int TK, int NS, int NW, int KS, int MODE>
+bool lds_fits(size_t dyn) {
+  static size_t static_bytes = [] {
+    hipFuncAttributes attr{};
+    const void* f = reinterpret_cast<const void*>(&verify_attn_kernel<D, NW, NWC, QB, TK, NS, KS, MODE, false>);
+    return hipFuncGetAttributes(&attr, f) == hipSuccess ? attr.sharedSizeBytes : kLdsPerWorkgroup;
+  }();
+  return static_bytes + dyn <= kLdsPerWorkgroup;
+}
+
 template <int D, int MODE>
 hipError_t launch_d_default(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   if (p.nwc == 1) return launch_variant<D, 1, 1, 64, 2, 4, 1, MODE>(a, stream);
   if (p.nwc == 2) return launch_variant<D, 2, 1, 64, 2, 4, 1, MODE>(a, stream);
   if (p.qb == 2) {
     if constexpr (D == 128) {
-      if (p.pipe == 7) return launch_variant<D, 4, 2, 64, 2, 8, 2, MODE>(a, stream);
+      // the 128-key ring leaves ~28 KB: a larger fused RoPE table (more than
+      // 27 positions) takes the 64-key form of the same two-wave layout
+      const size_t dyn = MODE == kModeTauRope ? rope_table_bytes(a) : 0;
+      if (p.pipe == 9 && lds_fits<D, 4, 2, 128, 2, 8, 2, MODE>(dyn))
+        return launch_variant<D, 4, 2, 128, 2, 8, 2, MODE>(a, stream);
+      if (p.pipe == 7 || p.pipe == 9) return launch_variant<D, 4, 2, 64, 2, 8, 2, MODE>(a, stream);
     }
     return launch_variant<D, 4, 2, 64, 2, 4, 1, MODE>(a, stream);
   }
@@ -915,6 +934,7 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
         case 6: return launch_variant<D, 8, 1, 64, 3, 8>(a, stream);
         case 7: return launch_variant<D, 4, 2, 64, 2, 8, 2>(a, stream);
         case 8: return launch_variant<D, 4, 2, 64, 3, 8, 2>(a, stream);
+        case 9: return launch_variant<D, 4, 2, 128, 2, 8, 2>(a, stream);
         default: return launch_variant<D, 4, 2, 64, 2>(a, stream);
       }
     }
@@ -992,15 +1012,17 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
   // 64x3, 64x4 with two waves per row group. 128 rows: 0 = 4 waves x 2 row
   // blocks 64x2, 1 = 4x2 32x4, 2 = 4x2 64x3, 3 = 8 waves x 1 32x4, 4 = 8x1
   // 64x2, 5 = 8x1 32x6, 6 = 8x1 64x3, 7 = 4x2 64x2 with two waves per row
-  // group, 8 = the same 64x3. With one 64-row workgroup per CU the deeper 32x4
-  // ring keeps more bytes in flight; with two per CU the other workgroup covers
-  // the latency and 64-key tiles halve the barriers. A 128-row workgroup
-  // carries twice the MFMA and softmax work per byte; alone on its CU it runs
-  // best with two waves per row group on every SIMD, each taking half of every
-  // key tile, so one wave's MFMA work overlaps the other's softmax (b16: 116
-  // vs 119 us, measured interleaved on two boxes).
+  // group, 8 = the same 64x3, 9 = the same 128x2. With one 64-row workgroup
+  // per CU the deeper 32x4 ring keeps more bytes in flight; with two per CU
+  // the other workgroup covers the latency and 64-key tiles halve the
+  // barriers. A 128-row workgroup carries twice the MFMA and softmax work per
+  // byte; alone on its CU it runs best with two waves per row group on every
+  // SIMD, each taking half of every key tile, so one wave's MFMA work overlaps
+  // the other's softmax, and with 128-key tiles, which halve the barriers per
+  // byte (b16, interleaved runs: 110.5 us vs 114.1 with 64-key tiles and
+  // 116-119 with one wave per row group).
   const long wgs = units * nsplit;
-  const int pipe_default = p.qb == 1 ? (wgs > 256 ? 1 : 0) : (wgs <= 256 ? 7 : 0);
+  const int pipe_default = p.qb == 1 ? (wgs > 256 ? 1 : 0) : (wgs <= 256 ? 9 : 0);
   p.pipe = env_int("SIMSD_ATTN_PIPE", pipe_default);
   p.chunk = chunk;
   p.nsplit = nsplit;
