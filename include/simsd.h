@@ -342,19 +342,20 @@ size_t simsd_accept_logits_workspace(int b, int B, int V);
  *                    cache_lens[s] are in use. Only the appended rows are
  *                    written.
  *   cache_offsets    int32 [b+1], non-decreasing, region bounds
- *   cache_lens       int32 [b], updated in place (written by a second launch
- *                    on the same stream, after every row has been copied).
- *                    Laid out right after the region bounds (cache_lens =
- *                    cache_offsets + b + 1), the same array serves as the
- *                    prefix_offsets of simsd_verify_attention with
- *                    SIMSD_PREFIX_LENS and as the start_pos of the next round.
+ *   cache_lens       int32 [b], updated in place (each sequence's length is
+ *                    read and advanced by the one workgroup that copies its
+ *                    rows). Laid out right after the region bounds
+ *                    (cache_lens = cache_offsets + b + 1), the same array
+ *                    serves as the prefix_offsets of simsd_verify_attention
+ *                    with SIMSD_PREFIX_LENS and as the start_pos of the next
+ *                    round.
  *   flags            SIMSD_KV_HEAD_MAJOR or 0
  *   status           optional int32 [b]; SIMSD_DEV_BAD_TAU or
  *                    SIMSD_DEV_COMMIT_OVERFLOW (L outside 0..B, a negative
  *                    length, or L more rows do not fit the region): nothing of
  *                    that sequence is written and its length is kept.
  * The cache must not overlap k_blk / v_blk, and cache_lens must not overlap
- * tau or accept_len.
+ * tau, accept_len or cache_offsets (SIMSD_ERR_ALIAS).
  * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, Hkv<1), _HEAD_DIM,
  * _FLAGS, _ALIGN (bf16 tensors 16-byte aligned), _LAUNCH.
  */

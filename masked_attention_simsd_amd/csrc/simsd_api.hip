@@ -345,14 +345,16 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
   if (flags & ~SIMSD_KV_HEAD_MAJOR) return SIMSD_ERR_FLAGS;
   if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
     return SIMSD_ERR_ALIGN;
-  // the lengths are read by every copy and then rewritten: they must not be
-  // one of the other inputs (the cache and the block are the caller's to keep apart)
+  // each workgroup rewrites its sequence's length after reading its inputs:
+  // the lengths must not be one of the inputs another workgroup reads (the
+  // cache and the block are the caller's to keep apart)
   auto overlap = [](const void* x, size_t nx, const void* y, size_t ny) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
     return a0 < b0 + ny && b0 < a0 + nx;
   };
   const size_t nl = static_cast<size_t>(b) * 4;
-  if (overlap(cache_lens, nl, tau, nl * B) || overlap(cache_lens, nl, accept_len, nl))
+  if (overlap(cache_lens, nl, tau, nl * B) || overlap(cache_lens, nl, accept_len, nl) ||
+      overlap(cache_lens, nl, cache_offsets, nl + 4))
     return SIMSD_ERR_ALIAS;
   simsd::CommitArgs a{};
   a.k_blk = static_cast<const uint16_t*>(k_blk);

@@ -214,3 +214,4 @@ def test_commit_kv_host_errors(lib):
     # the lengths may not be tau or accept_len (they are rewritten after every copy read them)
     assert f(lens=ctypes.c_void_p(0x200010)) == 10
     assert f(lens=ctypes.c_void_p(0x300000)) == 10
+    assert f(lens=ctypes.c_void_p(0x400008)) == 10  # inside cache_offsets
