@@ -338,8 +338,8 @@ def main():
     acc_logits_us = alone(lib.simsd_accept_logits, 4) * 1e6
     rope_us = alone(lib.simsd_rope_copy, 0) * 1e6
     # KV commit of set 0's accepted drafts, appended call after call to a
-    # head-major cache whose regions have room for every call (two launches:
-    # the row copies, then the length update)
+    # head-major cache whose regions have room for every call (one launch per
+    # call: each sequence's workgroup copies its rows and advances its length)
     n_commit = min(args.steps, 200)
     cap = (n_commit + 1) * B
     kc = torch.empty(Hkv, b * cap, d, dtype=torch.bfloat16, device=dev)

@@ -238,6 +238,9 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   if (wave == 0) {
     const int t_k = lane < B ? a.tau[static_cast<size_t>(s) * B + lane] : 0;  // tau(lane+1)
     const int x_k = lane < B ? a.draft[static_cast<size_t>(s) * B + lane] : 0;
+    // u_t of temporal step t = lane + 1, requested with tau and the drafts so
+    // that its latency is not paid after the gathers
+    const float u_t = lane < B ? a.u[static_cast<size_t>(s) * (B + 1) + lane] : 0.0f;
     if (lane < B) inv_s[lane] = -1;
     // invert: position k = lane writes itself at slot tau(k) - 1; a duplicate or
     // out-of-range label makes tau invalid
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
             r = pa > 0.0f ? 1.0f : 0.0f;
           }
         }
-        acc = a.u[static_cast<size_t>(s) * (B + 1) + lane] < r;
+        acc = u_t < r;
       }
       const unsigned long long rej = __ballot(lane < B && !acc);
       const int L = rej ? __ffsll(static_cast<long long>(rej)) - 1 : B;

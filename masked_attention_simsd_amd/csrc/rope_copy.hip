@@ -23,6 +23,7 @@ namespace simsd {
 namespace {
 
 constexpr int kRopeThreads = 256;
+typedef __attribute__((address_space(1))) uint16_t gu16;  // global memory
 constexpr int kMaxHalf = 64;  // d <= 128
 
 // One thread rotates 4 consecutive pairs of one head row: rotate-half pairs
@@ -34,15 +35,16 @@ struct Pairs4 {
 };
 
 __device__ __forceinline__ Pairs4 load4(const uint16_t* row, int i0, int half, bool interleaved) {
+  // two 8-byte pieces in either layout (rotate-half: elements i0.. and
+  // half+i0..; interleaved: the 16 contiguous bytes from 2 i0), so the number
+  // of loads does not depend on the layout and the angle inputs loaded before
+  // them can be waited for alone
+  const int o0 = interleaved ? 2 * i0 : i0;
+  const int o1 = interleaved ? 2 * i0 + 4 : half + i0;
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + o0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(row + o1);
   Pairs4 v;
-  if (!interleaved) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + i0);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + half + i0);
-    v.w[0] = lo.x, v.w[1] = lo.y, v.w[2] = hi.x, v.w[3] = hi.y;
-  } else {
-    const uint4 a = *reinterpret_cast<const uint4*>(row + 2 * i0);
-    v.w[0] = a.x, v.w[1] = a.y, v.w[2] = a.z, v.w[3] = a.w;
-  }
+  v.w[0] = lo.x, v.w[1] = lo.y, v.w[2] = hi.x, v.w[3] = hi.y;
   return v;
 }
 
@@ -91,18 +93,32 @@ __global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a, int
   const int nh = min(heads_per_wg, heads - h0);
   const int items = 2 * nh * groups;
   const bool active = tid < items;  // heads_per_wg is chosen so items <= blockDim
-  const int grp = tid % groups;
-  const int hh = h0 + (tid / groups) % nh;
-  const int slot = tid / (groups * nh);  // 0: D_k, 1: D~_k
+  // threads past the items load item 0's row (never stored): every load is
+  // unconditional, so the wait for the angle inputs can leave the rows in flight
+  const int it = active ? tid : 0;
+  const int grp = it % groups;
+  const int hh = h0 + (it / groups) % nh;
+  const int slot = it / (groups * nh);  // 0: D_k, 1: D~_k
   const int r = k + slot * a.B;
-  uint16_t* row = hh < a.Hq ? a.q + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hq + hh) * a.d
-                            : a.k + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hkv + (hh - a.Hq)) * a.d;
-  Pairs4 v{};
-  if (active) v = load4(row, grp * 4, half, a.interleaved != 0);
-
+  // The angle inputs (this thread's frequency, the sequence's start position)
+  // are requested before the row, so that waiting for them does not also wait
+  // for the row (loads complete in issue order) and the fp64 angle evaluation
+  // overlaps the row's latency.
+  const double inv_freq = a.inv_freq[min(tid, half - 1)];
   const long pos_d = static_cast<long>(a.start_pos[s]) + k;
+  // The two base pointers are pinned to scalar registers before the per-lane
+  // select: selecting between the two argument slots instead would turn into a
+  // per-lane load of the pointer itself, a full memory round trip before the
+  // row load can be issued.
+  gu16* qbase = (gu16*)a.q;
+  gu16* kbase = (gu16*)a.k;
+  asm volatile("" : "+s"(qbase), "+s"(kbase));
+  gu16* grow = hh < a.Hq ? qbase + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hq + hh) * a.d
+                         : kbase + ((static_cast<size_t>(s) * 2 * a.B + r) * a.Hkv + (hh - a.Hq)) * a.d;
+  uint16_t* row = (uint16_t*)grow;
+  const Pairs4 v = load4(row, grp * 4, half, a.interleaved != 0);
+
   if (tid < half) {
-    const double inv_freq = a.inv_freq[tid];
     double ang = static_cast<double>(pos_d) * inv_freq;
     sincos(ang, &sn_d[tid], &cs_d[tid]);
     if (a.no_copy) {
