@@ -86,6 +86,13 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory");
 }
 
+// 4 bytes HBM -> LDS (global_load_lds_dword): lane l reads sbase + voff and
+// its word lands at LDS byte address m0 + 4 * l.
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Buffer descriptor over [base, base + bytes) for device-coherent (sc1) 8- and
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   static_assert(IPW >= 1 && (TK / RPI) % NW == 0 && NWC * KS <= NW, "tile / wave mismatch");
   static_assert(TKW % 32 == 0 && (KS == 1 || KS == 2), "key slice per wave");
   static_assert(KS == 1 || NWC * QB * (D / 16) * 64 * 16 <= NS * STAGE_B, "state exchange fits the ring");
-  static_assert(NS >= 2 && (NS - 2) * DPW < 64, "pipeline depth");
+  static_assert(NS >= 2 && (NS - 1) * DPW < 64, "pipeline depth");
   static_assert(NS * STAGE_B <= 150 * 1024, "LDS ring");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE_B];
@@ -278,27 +285,97 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   const int o0 = a.offsets[s];
   const int cap = a.offsets[s + 1] - o0;
   int P = a.prefix_lens[s] - (a.prefix_lens_are_ends ? o0 : 0);
+  // read before the first DMA is issued, so it can be a scalar load (the DMA
+  // asm clobbers memory as far as the compiler knows)
+  const long pos0 = ROPE ? static_cast<long>(a.start_pos[s]) : 0;
+  const int rows_total = a.offsets[a.b];  // rows of a head-major cache per KV head
+
+  // ---- tau, the workgroup's query rows (and the RoPE frequencies) ----
+  // Staged into LDS by DMA at kernel entry when the rows fit one ring stage
+  // (every default plan): tau into tau_s, the MWG query rows into ring slot
+  // NS - 1, which the ring first fills at the first pipeline step, and with
+  // fused RoPE the frequencies (kernel arguments) behind the cos/sin table.
+  // Their addresses need no loaded value, so they are requested before the
+  // prefix bounds arrive; loads complete in issue order, so the later wait
+  // for them leaves the first key tiles in flight, and the work between that
+  // wait and the first tile (table, query rotation, mask bits) overlaps the
+  // ring fill. (Plain loads would need a compiler wait for every outstanding
+  // load, the ring DMA included.) Rows past the unit's M rows take a copy of
+  // its last row: their results are never stored. Query rows sit row-major in
+  // LDS with their 16-byte chunks XOR-swizzled by row, so the 16 rows one read
+  // instruction touches hit distinct banks.
+  const bool computes = wave < NWC * KS;
+  const int rw = wave % NWC;   // row group
+  const int kh = wave / NWC;   // key slice of every tile (KS = 2)
+  const bool owner = computes && kh == 0;  // finishes the rows after the loop
+  const int kw0 = kh * TKW;                // first key of this wave's slice of a tile
+  constexpr bool QDMA = MWG * ROW_B <= STAGE_B;
+  static_assert(QDMA || !ROPE, "fused RoPE stages its query rows by DMA");
+  constexpr int NQI = MWG * ROW_B / 1024;  // DMA instructions for the query rows
+  constexpr int QPW = (NQI + NW - 1) / NW;  // ... per wave (the last one repeated to even them out)
+  SIMSD_LDS uint8_t* const ring_l = (SIMSD_LDS uint8_t*)ring;
+  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_l));
+  SIMSD_LDS uint8_t* const q_st = ring_l + (NS - 1) * STAGE_B;
+  // fused RoPE: the table's (cos, sin) pairs, then the staged frequencies
+  const int rope_npos = ROPE ? (a.rope_no_copy ? twoB : B) : 0;
+  double* const rope_freq = rope_tab + static_cast<size_t>(rope_npos) * D;
+  bf16x8 qreg[QB][KK];
+  int r_q[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int m = min(slice * MWG + (rw * QB + qb) * 16 + n16, a.M - 1);
+    r_q[qb] = a.row0 + m / a.G;
+  }
+  int tau_ld = 0;
+  if constexpr (QDMA) {
+    if (wave == 0) {
+      if constexpr (ROPE) {
+        // the D/2 fp64 frequencies: 16 bytes per lane, lanes past them repeat the last piece
+        const char* kargs = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+        dma16(kargs + offsetof(AttnArgs, rope_inv_freq), 16u * static_cast<uint32_t>(min(lane, D / 4 - 1)),
+              static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIMSD_LDS double*)rope_freq)));
+      }
+      if constexpr (!MASK) {
+        const int* tau_row = a.tau + static_cast<size_t>(s) * B;
+        dma4(tau_row, 4u * static_cast<uint32_t>(min(lane, B - 1)),
+             static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIMSD_LDS int*)tau_s)));
+      }
+    }
+    const uint16_t* q_seq = a.q_blk + static_cast<size_t>(s) * twoB * a.Hq * D;
+    const uint32_t q_lds = ring_base + static_cast<uint32_t>((NS - 1) * STAGE_B);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int gi = min(i * NW + wave, NQI - 1);
+      const int row = gi * RPI + lane / CH;  // query row of the workgroup
+      const int p = lane % CH;               // LDS chunk slot this lane fills
+      const int m = min(slice * MWG + row, a.M - 1);
+      const int r = a.row0 + m / a.G;
+      const int h = g * a.G + m % a.G;
+      const uint32_t src = static_cast<uint32_t>((r * a.Hq + h) * D) * 2u +
+                           16u * static_cast<uint32_t>(p ^ (row & (CH - 1)));
+      dma16(q_seq, src, q_lds + static_cast<uint32_t>(gi * 1024));
+    }
+  }
+
   const int lim = min(a.max_prefix, max(cap, 0));
   const bool bad_prefix = P < 0 || P > lim;
   P = P < 0 ? 0 : (P > lim ? lim : P);
   const int ns = P > 0 ? (P + a.chunk - 1) / a.chunk : 1;
-  if (split >= ns) return;
+  if (split >= ns) {
+    if constexpr (QDMA) wait_vmcnt<0>();  // no DMA may land in LDS after the workgroup ends
+    return;
+  }
   // split 0 also takes the block tiles, so its prefix run is `shift` keys
   // shorter and every later boundary moves down by as much; the last split
   // runs to the end of the prefix
   const int key_lo = split == 0 ? 0 : split * a.chunk - a.shift;
   const int key_hi = split == ns - 1 ? P : (split + 1) * a.chunk - a.shift;
 
-  // read before the first DMA is issued, so it can be a scalar load (the DMA
-  // asm clobbers memory as far as the compiler knows)
-  const long pos0 = ROPE ? static_cast<long>(a.start_pos[s]) : 0;
-
   // ---- tile schedule: (split 0) the block tiles, then the prefix tiles of this chunk ----
   // prefix rows of (s, g): token-major [sum P][Hkv][d] or head-major [Hkv][sum P][d]
   const uint32_t rsb = a.kv_head_major ? ROW_B : static_cast<uint32_t>(a.Hkv) * ROW_B;  // bytes between rows
-  const size_t pre0 = a.kv_head_major
-                          ? (static_cast<size_t>(g) * a.offsets[a.b] + a.offsets[s]) * D
-                          : (static_cast<size_t>(a.offsets[s]) * a.Hkv + g) * D;
+  const size_t pre0 = a.kv_head_major ? (static_cast<size_t>(g) * rows_total + o0) * D
+                                      : (static_cast<size_t>(o0) * a.Hkv + g) * D;
   const char* kpre = reinterpret_cast<const char*>(a.k_pre + pre0);
   const char* vpre = reinterpret_cast<const char*>(a.v_pre + pre0);
   const uint32_t rsb_blk = static_cast<uint32_t>(a.Hkv) * ROW_B;  // block rows are [2B][Hkv][d]
@@ -317,9 +394,6 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     const int j = t - n_blk + rot;
     return j >= n_pre ? j - n_pre : j;
   };
-  SIMSD_LDS uint8_t* const ring_l = (SIMSD_LDS uint8_t*)ring;
-  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring_l));
-
   // Per-lane byte offsets of the DMA of a full prefix tile: instruction i of
   // this wave fills LDS rows gi*RPI .. gi*RPI+RPI-1 (gi = NW i + wave); lane l
   // supplies the chunk that the swizzle places in LDS slot l % CH of its row.
@@ -366,31 +440,21 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   for (int t = 0; t < NS - 1; ++t)
     if (t < ntiles) issue(t);
 
-  // ---- tau and this lane's queries, requested right behind the first tiles
-  // (nothing before the ring fill waits on memory): one query per 16-row
-  // block, row m of the unit ----
-  const bool computes = wave < NWC * KS;
-  const int rw = wave % NWC;   // row group
-  const int kh = wave / NWC;   // key slice of every tile (KS = 2)
-  const bool owner = computes && kh == 0;  // finishes the rows after the loop
-  const int kw0 = kh * TKW;                // first key of this wave's slice of a tile
-  const int tau_ld = (!MASK && tid < B) ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
-  // Lanes past the unit's M rows load (and later compute) a copy of its last
-  // row: their results are never stored, and unconditional loads keep the
-  // compiler from waiting on them (and so on the DMA ring) right here.
-  bf16x8 qreg[QB][KK];
-  int r_q[QB];
+  if constexpr (!QDMA) {
+    // Plain loads, requested right behind the first tiles (the compiler's
+    // wait for them also waits for those tiles).
+    tau_ld = (!MASK && tid < B) ? a.tau[static_cast<size_t>(s) * B + tid] : 0;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int m = min(slice * MWG + (rw * QB + qb) * 16 + n16, a.M - 1);
-    const int r = a.row0 + m / a.G;
-    const int h = g * a.G + m % a.G;
-    const uint16_t* qrow = a.q_blk + ((static_cast<size_t>(s) * twoB + r) * a.Hq + h) * D;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int m = min(slice * MWG + (rw * QB + qb) * 16 + n16, a.M - 1);
+      const int h = g * a.G + m % a.G;
+      const uint16_t* qrow = a.q_blk + ((static_cast<size_t>(s) * twoB + r_q[qb]) * a.Hq + h) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qreg[qb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * a16));
-    r_q[qb] = r;
+      for (int kk = 0; kk < KK; ++kk)
+        qreg[qb][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * a16));
+    }
   }
+
   // explicit mask: this lane's rows' mask words (<= 128 block keys), requested
   // with the queries (split 0 only: it takes the block tiles)
   // (two arrays, not one of pairs: a pair selected by a runtime condition
@@ -406,20 +470,41 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (QDMA) {
+    // tau and the query rows have landed; the first tiles may stay in flight
+    wait_tile<DPW, NS - 1>(min(NS - 1, ntiles));
+  } else {
+    if (tid < 64) tau_s[tid] = tau_ld;
+  }
+  wait_lgkm0();
+  block_barrier();  // tau_s, the query rows (and the RoPE frequencies) visible
+  if constexpr (QDMA) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = (rw * QB + qb) * 16 + n16;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        union {
+          u32x4 u;
+          bf16x8 b;
+        } qv;
+        qv.u = *reinterpret_cast<SIMSD_LDS const u32x4*>(q_st + row * ROW_B + 16 * ((4 * kk + a16) ^ (row & (CH - 1))));
+        qreg[qb][kk] = qv.b;
+      }
+    }
+    // complete before the first pipeline step refills this slot
+    wait_lgkm0();
+  }
   if constexpr (ROPE) {
     // cos/sin of every (block position, frequency) this workgroup needs,
     // computed while the first tiles are in flight. Row p of the table is
     // position start + p: the B data positions, then (without the copy rule)
     // the B positions after them that the mask slots take instead. Entry e of
-    // the table has frequency e % (D/2) = lane % (D/2); each lane picks its
-    // frequency out of the kernel arguments with uniform (scalar) loads, so no
-    // vector load (whose wait would also drain the DMA ring) is needed here.
-    double inv_l = 0.0;
-#pragma unroll
-    for (int k = 0; k < 64; ++k) inv_l = lane == k ? a.rope_inv_freq[k % (D / 2)] : inv_l;
-    const int npos = a.rope_no_copy ? twoB : B;
+    // the table has frequency e % (D/2) = lane % (D/2), read from the staged
+    // frequencies.
+    const double inv_l = rope_freq[lane % (D / 2)];
     static_assert((NW * 64) % (D / 2) == 0, "table entries keep the lane's frequency");
-    for (int e = tid; e < npos * (D / 2); e += NW * 64) {
+    for (int e = tid; e < rope_npos * (D / 2); e += NW * 64) {
       const int pi = e / (D / 2);
       const double ang = static_cast<double>(pos0 + pi) * inv_l;
       double sn, cs;
@@ -427,11 +512,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
       rope_tab[2 * e] = cs;
       rope_tab[2 * e + 1] = sn;
     }
+    wait_lgkm0();
+    block_barrier();  // the table visible
   }
-
-  if (tid < 64) tau_s[tid] = tau_ld;
-  wait_lgkm0();
-  block_barrier();  // tau_s (and the RoPE table) visible
   if (a.status && split == 0 && slice == 0 && g == 0 && wave == 0) {
     int cnt = 0;
     if (lane < B)
@@ -478,10 +561,12 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 
   // Make the compiler complete the Q loads here, not at their first use inside
   // the tile loop (a wait there would also drain the DMA ring every tile).
+  if constexpr (!QDMA) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qreg[qb][kk]));
+      for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qreg[qb][kk]));
+  }
 
   const float c2 = a.scale_log2;  // softmax scale * log2(e)
   f32x4 oacc[QB][DB];
@@ -861,11 +946,13 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   }
 }
 
-// Bytes of the fused RoPE table: (cos, sin) fp64 per (position, frequency).
+// Dynamic LDS of the fused RoPE path: the (cos, sin) fp64 table per
+// (position, frequency) and the staged frequencies.
 inline size_t rope_table_bytes(const AttnArgs& a) {
   if (!a.rope) return 0;
   const int npos = a.rope_no_copy ? 2 * a.B : a.B;
-  return static_cast<size_t>(npos) * (a.d / 2) * 2 * sizeof(double);
+  // the table, then 1 KB where one wave's DMA stages the frequencies
+  return static_cast<size_t>(npos) * (a.d / 2) * 2 * sizeof(double) + 1024;
 }
 
 template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1, int MODE = kModeTau>
@@ -904,7 +991,8 @@ hipError_t launch_d_default(const AttnArgs& a, const AttnPlan& p, hipStream_t st
   if (p.qb == 2) {
     if constexpr (D == 128) {
       // the 128-key ring leaves ~28 KB: a larger fused RoPE table (more than
-      // 27 positions) takes the 64-key form of the same two-wave layout
+      // 26 positions, with the staged frequencies) takes the 64-key form of
+      // the same two-wave layout
       const size_t dyn = MODE == kModeTauRope ? rope_table_bytes(a) : 0;
       if (p.pipe == 9 && lds_fits<D, 4, 2, 128, 2, 8, 2, MODE>(dyn))
         return launch_variant<D, 4, 2, 128, 2, 8, 2, MODE>(a, stream);
