@@ -159,12 +159,9 @@ __device__ __forceinline__ int swz_v(int row) {
 }
 
 // Temporal mask between block rows, branch-free: query with slot flag / label,
-// key block row c in [0, 2B) (c < B: data token D_{c+1}; else mask slot
-// D~_{c-B+1}).
-__device__ __forceinline__ bool block_allowed(bool q_slot, int tau_q, int c, int B,
-                                              const int* tau_s, int data_rule) {
-  const bool k_slot = c >= B;
-  const int tau_k = tau_s[k_slot ? c - B : c];
+// key block row with slot flag / label (a data token D_j or mask slot D~_j,
+// label tau(j)).
+__device__ __forceinline__ bool block_allowed(bool q_slot, int tau_q, bool k_slot, int tau_k, int data_rule) {
   const bool slot_row = k_slot ? (tau_k >= tau_q) : (tau_k < tau_q);
   const bool data_row = !k_slot && (data_rule == 1 || tau_k <= tau_q);
   return q_slot ? slot_row : data_row;
@@ -516,10 +513,16 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     block_barrier();  // the table visible
   }
   if (a.status && split == 0 && slice == 0 && g == 0 && wave == 0) {
-    int cnt = 0;
-    if (lane < B)
-      for (int k = 0; k < B; ++k) cnt += tau_s[k] == lane + 1;
-    const bool bad_tau = __ballot(lane < B && cnt != 1) != 0ull;
+    // tau is a permutation of 1..B iff every label is in range and the OR of
+    // the label bits over the B lanes has all B bits set (a duplicate leaves
+    // one unset); one LDS read and a wave OR, no loop over the labels
+    const int t = lane < B ? tau_s[lane] : 1;
+    const bool in_range = t >= 1 && t <= B;
+    uint64_t bit = (lane < B && in_range) ? (1ull << (t - 1)) : 0ull;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bit |= __shfl_xor(bit, off, kWave);
+    const uint64_t full = B >= 64 ? ~0ull : ((1ull << B) - 1ull);
+    const bool bad_tau = (__ballot(!in_range) != 0ull) || bit != full;
     if (lane == 0 && (bad_tau || bad_prefix))
       atomicOr(&a.status[s], (bad_tau ? kDevBadTau : 0) | (bad_prefix ? kDevBadPrefix : 0));
   }
@@ -537,13 +540,27 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   // (while the first tiles are in flight): bit (bt * NKB * 4 + kb * 4 + i) is
   // key kw0 + 32(kb/2) + 8 a16 + 4(kb%2) + i of block tile bt, set if allowed.
   static_assert(((128 + TK - 1) / TK) * NKB * 4 <= 64, "block mask bits");
+  // Per block tile, the labels of this lane's keys are read from LDS together
+  // (clamped indices, no branch around the reads, so one wait covers them),
+  // then every query block takes its bits from them.
   uint64_t blk_bits[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    blk_bits[qb] = 0;
-    if (split == 0 && computes) {
-      const int nbt = (twoB + TK - 1) / TK;
-      for (int bt = 0; bt < nbt; ++bt)
+  for (int qb = 0; qb < QB; ++qb) blk_bits[qb] = 0;
+  if (split == 0 && computes) {
+    const int nbt = (twoB + TK - 1) / TK;
+    for (int bt = 0; bt < nbt; ++bt) {
+      int tau_k[NKB][4];
+      if constexpr (!MASK) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = min(bt * TK + kw0 + 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i, twoB - 1);
+            tau_k[kb][i] = tau_s[c >= B ? c - B : c];
+          }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -553,7 +570,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
             if constexpr (MASK)
               ok = c < twoB && (((c >= 64 ? mhi[qb] : mlo[qb]) >> (c & 63)) & 1ull) != 0;
             else
-              ok = c < twoB && block_allowed(slot_q[qb], tau_q[qb], c, B, tau_s, a.data_rule);
+              ok = c < twoB && block_allowed(slot_q[qb], tau_q[qb], c >= B, tau_k[kb][i], a.data_rule);
             if (ok) blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
           }
     }
