@@ -167,6 +167,14 @@ __device__ __forceinline__ bool block_allowed(bool q_slot, int tau_q, bool k_slo
   return q_slot ? slot_row : data_row;
 }
 
+// Doubles per row of the fused-RoPE cos/sin table: D/2 (cos, sin) pairs plus
+// one pad pair, so that rows a bank period apart (D * 8 bytes) do not map to
+// the same LDS banks when lanes of different rows read the same frequency.
+template <int D>
+__host__ __device__ constexpr int rope_row_doubles() {
+  return D + 2;
+}
+
 // RoPE-copy table row of block row r: data row D_{r+1} and (with the copy
 // rule) mask slot D~_{r-B+1} share position r resp. r - B; without the copy
 // rule the slot keeps its own row r (position start + r).
@@ -181,7 +189,7 @@ __device__ __forceinline__ int rope_pos_row(int r, int B, int no_copy) {
 template <int D, int KK>
 __device__ __forceinline__ void rope_rows(bf16x8 (&x)[KK], int pr, int a16, int interleaved,
                                           const double* tab) {
-  const double* t = tab + static_cast<size_t>(pr) * D;  // D/2 (cos, sin) pairs
+  const double* t = tab + static_cast<size_t>(pr) * rope_row_doubles<D>();  // D/2 (cos, sin) pairs
   union U {
     bf16x8 b;
     uint16_t h[8];
@@ -256,7 +264,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   __shared__ float xml[KS == 2 ? NWC * QB * 64 * 2 : 1];  // (m, l) handed between key slices
   __shared__ int tau_s[64];
   __shared__ int last_s;
-  extern __shared__ double rope_tab[];  // ROPE: [position][d/2] x (cos, sin)
+  extern __shared__ double rope_tab[];  // ROPE: [position][d/2] x (cos, sin), rows padded
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps DMA math scalar
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   SIMSD_LDS uint8_t* const q_st = ring_l + (NS - 1) * STAGE_B;
   // fused RoPE: the table's (cos, sin) pairs, then the staged frequencies
   const int rope_npos = ROPE ? (a.rope_no_copy ? twoB : B) : 0;
-  double* const rope_freq = rope_tab + static_cast<size_t>(rope_npos) * D;
+  double* const rope_freq = rope_tab + static_cast<size_t>(rope_npos) * rope_row_doubles<D>();
   bf16x8 qreg[QB][KK];
   int r_q[QB];
 #pragma unroll
@@ -506,8 +514,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
       const double ang = static_cast<double>(pos0 + pi) * inv_l;
       double sn, cs;
       sincos(ang, &sn, &cs);
-      rope_tab[2 * e] = cs;
-      rope_tab[2 * e + 1] = sn;
+      const int f = e - pi * (D / 2);  // frequency index
+      rope_tab[pi * rope_row_doubles<D>() + 2 * f] = cs;
+      rope_tab[pi * rope_row_doubles<D>() + 2 * f + 1] = sn;
     }
     wait_lgkm0();
     block_barrier();  // the table visible
@@ -727,7 +736,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
       const int c = r0 + row;
       if (c >= twoB) continue;
       const int sw = swz_k<D>(row);
-      const double* tr = rope_tab + static_cast<size_t>(rope_pos_row(c, B, a.rope_no_copy)) * D;
+      const double* tr = rope_tab + static_cast<size_t>(rope_pos_row(c, B, a.rope_no_copy)) * rope_row_doubles<D>();
       union U {
         u32x4 u;
         uint16_t h[8];
@@ -968,8 +977,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 inline size_t rope_table_bytes(const AttnArgs& a) {
   if (!a.rope) return 0;
   const int npos = a.rope_no_copy ? 2 * a.B : a.B;
-  // the table, then 1 KB where one wave's DMA stages the frequencies
-  return static_cast<size_t>(npos) * (a.d / 2) * 2 * sizeof(double) + 1024;
+  // the table (padded rows), then 1 KB where one wave's DMA stages the frequencies
+  const int row = a.d == 64 ? rope_row_doubles<64>() : rope_row_doubles<128>();
+  return static_cast<size_t>(npos) * row * sizeof(double) + 1024;
 }
 
 template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1, int MODE = kModeTau>
