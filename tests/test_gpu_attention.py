@@ -163,19 +163,20 @@ def test_deterministic_and_split_independent():
 
 
 def test_status_bits():
-    w = synth.custom(b=3, Hq=4, Hkv=2, d=64, B=4, prefix=(50, 90))
+    # tau not a permutation of 1..B: a repeated label, a label 0, a label past B
+    w = synth.custom(b=4, Hq=4, Hkv=2, d=64, B=4, prefix=(50, 90))
     x = synth.make_inputs(w, with_accept=False, seed=5)
     x["tau"][1] = torch.tensor([1, 1, 2, 3], dtype=torch.int32)
-    status = torch.zeros(3, dtype=torch.int32, device="cuda")
+    x["tau"][2] = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    x["tau"][3] = torch.tensor([1, 2, 3, 5], dtype=torch.int32)
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
     lens = (x["prefix_offsets"][1:] - x["prefix_offsets"][:-1]).tolist()
     short = int(min(lens))
     run_gpu(x, status=status, max_prefix=short)
     st = status.cpu().tolist()
-    assert st[1] & binding.SIMSD_DEV_BAD_TAU
-    for s in range(3):
+    for s in range(4):
         assert bool(st[s] & binding.SIMSD_DEV_BAD_PREFIX) == (lens[s] > short)
-        if s != 1:
-            assert not st[s] & binding.SIMSD_DEV_BAD_TAU
+        assert bool(st[s] & binding.SIMSD_DEV_BAD_TAU) == (s != 0)
 
 
 def test_one_workspace_shared_by_calls_of_different_shapes():
