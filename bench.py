@@ -88,6 +88,20 @@ def counter_summary(workload, key):
         return None
 
 
+def host_cpu():
+    """The host's CPU model and logical core count (from /proc/cpuinfo), for
+    the CPU baseline's context."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "logical_cores": os.cpu_count()}
+
+
 def subset(x, n):
     """The inputs of the first n sequences (a bounded CPU sample)."""
     import dataclasses
@@ -291,6 +305,7 @@ def main():
             print("parity check failed; not timing", file=sys.stderr)
             sys.exit(1)
         cpu = {"value": round(cpu_bps, 3), "unit": "blocks/s", "cores": threads, "kind": "oracle",
+               "host": host_cpu(),
                "sample": f"{reps} full batches of the {workload} workload ({reps * b} blocks: "
                          f"RoPE-copy + verify attention + acceptance, fp64 C oracle) in {secs:.1f} s",
                "single_core": {"value": round(cpu1_bps, 3), "unit": "blocks/s",
