@@ -128,3 +128,18 @@ def test_fused_without_k_rot_and_status():
                                         g["prefix_offsets"], g["tau"], g["start_pos"], status=status)
     torch.cuda.synchronize()
     assert status.cpu().tolist() == [0, binding.SIMSD_DEV_BAD_TAU]
+
+
+@pytest.mark.parametrize("rflags", [0, binding.SIMSD_ROPE_NO_COPY])
+def test_fused_large_positions(rflags):
+    # positions near the int32 limit: the fused table takes the same
+    # large-argument sin/cos as the RoPE-copy kernel, bit for bit
+    w = synth.custom(b=2, Hq=32, Hkv=8, d=128, B=8, prefix=(100, 300))
+    x = synth.make_inputs(w, with_accept=False, seed=12)
+    x["start_pos"] = torch.tensor([2**31 - 20, 2**30 + 7], dtype=torch.int32)
+    say(f"fused large positions {x['start_pos'].tolist()} rflags={rflags}")
+    g = prep(x, False)
+    ref_out, ref_lse, ref_k = two_call(g, 10000.0, rflags, 0, 300)
+    out, lse, k_rot = fused(g, 10000.0, rflags, 0, 300)
+    torch.cuda.synchronize()
+    assert torch.equal(k_rot, ref_k) and torch.equal(out, ref_out) and torch.equal(lse, ref_lse)

@@ -64,3 +64,19 @@ def test_rope_d64_and_B1():
         binding.simsd_rope_copy(q, k, x["start_pos"].cuda(), 500.0, 0)
         _check(q, oracle.rope_copy(f64(x["q_blk"]), x["start_pos"].numpy(), base=500.0), "q")
         _check(k, oracle.rope_copy(f64(x["k_blk"]), x["start_pos"].numpy(), base=500.0), "k")
+
+
+@pytest.mark.parametrize("flags", [0, binding.SIMSD_ROPE_NO_COPY])
+def test_rope_large_positions(flags):
+    # angles beyond 2^30 rad (frequency 1 at positions near the int32 limit)
+    # take the large-argument reduction of the fp64 sin/cos
+    w = synth.custom(b=2, Hq=4, Hkv=2, d=128, B=8, prefix=(16, 16))
+    x = synth.make_inputs(w, with_accept=False, seed=11)
+    x["start_pos"] = torch.tensor([2**31 - 20, 2**30 + 7], dtype=torch.int32)
+    say(f"rope large positions {x['start_pos'].tolist()} flags={flags}")
+    q, k = x["q_blk"].cuda(), x["k_blk"].cuda()
+    binding.simsd_rope_copy(q, k, x["start_pos"].cuda(), 10000.0, flags)
+    torch.cuda.synchronize()
+    kw = dict(base=10000.0, no_copy=bool(flags & 2))
+    _check(q, oracle.rope_copy(f64(x["q_blk"]), x["start_pos"].numpy(), **kw), "q")
+    _check(k, oracle.rope_copy(f64(x["k_blk"]), x["start_pos"].numpy(), **kw), "k")
