@@ -221,6 +221,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     binding.load_library()  # fails loudly if libsimsd.so is missing
+    KV_LAYOUT = binding.SIMSD_KV_HEAD_MAJOR | binding.SIMSD_KV_PAIRED
     dev = torch.device("cuda:0")
     workload = args.workload
     x = synth.make_inputs(workload)
@@ -232,12 +233,21 @@ def main():
         args.sets = min(256, max(2, -(-MALL_EVICT_BYTES // kv_bytes)))
     log(f"workload {workload}: {w.describe()}; {args.sets} input sets")
 
-    # The prefix cache is stored head-major ([Hkv][sum P][d], SIMSD_KV_HEAD_MAJOR):
-    # each (sequence, KV head) split then streams one contiguous strip.
+    # The prefix cache is stored paired head-major ([Hkv][sum P][2][d]: the key
+    # row then the value row of each token, SIMSD_KV_HEAD_MAJOR | SIMSD_KV_PAIRED):
+    # each (sequence, KV head) split then streams one contiguous strip holding
+    # its keys and values together.
     base = {k: v.to(dev) for k, v in x.items() if torch.is_tensor(v)}
-    for key in ("k_pre", "v_pre"):
-        base[key] = base[key].transpose(0, 1).contiguous()
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.sets - 1)]
+    base["kv_pre"] = torch.stack([base["k_pre"].transpose(0, 1), base["v_pre"].transpose(0, 1)],
+                                 dim=2).contiguous()
+
+    def with_views(st):
+        st["k_pre"], st["v_pre"] = binding.kv_pair_views(st["kv_pre"])
+        return st
+
+    base = with_views(base)
+    sets = [base] + [with_views({k: v.clone() for k, v in base.items() if k not in ("k_pre", "v_pre")})
+                     for _ in range(args.sets - 1)]
     b, B, Hq, Hkv, d = w.b, w.B, w.Hq, w.Hkv, w.d
     outs = [torch.empty_like(s["q_blk"]) for s in sets]
     krots = [torch.empty_like(s["k_blk"]) for s in sets]
@@ -259,14 +269,14 @@ def main():
                 ctypes.c_float(w.rope_base), 0, hs)
         attn = (P(s["q_blk"]), P(s["k_blk"]), P(s["v_blk"]), P(s["k_pre"]), P(s["v_pre"]),
                 P(s["prefix_offsets"]), P(s["tau"]), P(outs[j]), None, b, B, Hq, Hkv, d,
-                max_prefix, ctypes.c_float(0.0), binding.SIMSD_KV_HEAD_MAJOR, None, P(ws),
+                max_prefix, ctypes.c_float(0.0), KV_LAYOUT, None, P(ws),
                 ws.numel(), hs)
         acc = (P(s["p"]), P(s["q"]), P(s["draft"]), P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]),
                P(Cs[j]), None, P(ws_acc), ws_acc.numel(), hs)
         fused = (P(s["q_blk"]), P(s["k_blk"]), P(s["v_blk"]), P(s["k_pre"]), P(s["v_pre"]),
                  P(s["prefix_offsets"]), P(s["tau"]), P(s["start_pos"]), ctypes.c_float(w.rope_base), 0,
                  P(krots[j]), P(outs[j]), None, b, B, Hq, Hkv, d, max_prefix, ctypes.c_float(0.0),
-                 binding.SIMSD_KV_HEAD_MAJOR, None, P(ws), ws.numel(), hs)
+                 KV_LAYOUT, None, P(ws), ws.numel(), hs)
         acc_logits = (P(s["target_logits"]), P(s["draft_logits"]), ctypes.c_float(1.0), P(s["draft"]),
                       P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]), P(Cs[j]), None, P(ws_accl),
                       ws_accl.numel(), hs)
@@ -353,16 +363,17 @@ def main():
     acc_logits_us = alone(lib.simsd_accept_logits, 4) * 1e6
     rope_us = alone(lib.simsd_rope_copy, 0) * 1e6
     # KV commit of set 0's accepted drafts, appended call after call to a
-    # head-major cache whose regions have room for every call (one launch per
-    # call: each sequence's workgroup copies its rows and advances its length)
+    # paired head-major cache whose regions have room for every call (one
+    # launch per call: each sequence's workgroup copies its rows and advances
+    # its length)
     n_commit = min(args.steps, 200)
     cap = (n_commit + 1) * B
-    kc = torch.empty(Hkv, b * cap, d, dtype=torch.bfloat16, device=dev)
-    vc = torch.empty_like(kc)
+    kvc = torch.empty(Hkv, b * cap, 2, d, dtype=torch.bfloat16, device=dev)
+    kc, vc = binding.kv_pair_views(kvc)
     ext = torch.cat([torch.arange(b + 1, dtype=torch.int32, device=dev) * cap,
                      torch.zeros(b, dtype=torch.int32, device=dev)])
     commit = (P(base["k_blk"]), P(base["v_blk"]), P(base["tau"]), P(Ls[0]), P(kc), P(vc), P(ext),
-              P(ext[b + 1:]), b, B, Hkv, d, binding.SIMSD_KV_HEAD_MAJOR, None, hs)
+              P(ext[b + 1:]), b, B, Hkv, d, KV_LAYOUT, None, hs)
     step(0)  # Ls[0]: the accepted lengths of set 0
     rows = int(Ls[0].sum().item())
     c0, c1 = ev(), ev()
@@ -408,7 +419,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{workload}: {w.describe()}", "global_batch": b,
                    "prefix": max_prefix, "block_B": B, "input_sets_rotated": args.sets,
-                   "kv_cache_layout": "head-major [Hkv][sum P][d]",
+                   "kv_cache_layout": "paired head-major [Hkv][sum P][2][d]",
                    "step": "rope_copy + verify_attention + accept"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -87,6 +87,12 @@ typedef enum {
 #define SIMSD_KV_HEAD_MAJOR 8u /* k_pre / v_pre are [Hkv][sum P][d] instead of [sum P][Hkv][d] */
 #define SIMSD_PREFIX_LENS 16u  /* prefix_offsets holds 2b+1 int32: b+1 region bounds, then b used
                                   lengths (a cache with room to grow; see simsd_commit_kv) */
+#define SIMSD_KV_PAIRED 32u    /* k_pre / v_pre (k_cache / v_cache for simsd_commit_kv) are the two
+                                  halves of one buffer whose innermost dims are [2][d], the key
+                                  row then the value row of each (token, KV head): [sum P][Hkv][2][d],
+                                  or [Hkv][sum P][2][d] with SIMSD_KV_HEAD_MAJOR. v_pre must equal
+                                  k_pre + d elements (else SIMSD_ERR_FLAGS). One tile's keys and
+                                  values are then one contiguous run (b16: ~5% faster streaming) */
 
 /*
  * simsd_rope_copy -- rotary position embedding of the block's queries and

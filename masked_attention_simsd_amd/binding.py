@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libsimsd.so")
 # flag and status values, as in include/simsd.h
 SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY = 0, 1, 2
 SIMSD_DATA_CAUSAL, SIMSD_DATA_BIDIR, SIMSD_DATA_SKIP, SIMSD_OUT_F32 = 0, 1, 2, 4
-SIMSD_KV_HEAD_MAJOR, SIMSD_PREFIX_LENS = 8, 16
+SIMSD_KV_HEAD_MAJOR, SIMSD_PREFIX_LENS, SIMSD_KV_PAIRED = 8, 16, 32
 SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
 SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
 SIMSD_DEV_COMMIT_OVERFLOW = 64
@@ -105,6 +105,35 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def kv_pair_views(kv):
+    """The key and value halves of a paired cache buffer (SIMSD_KV_PAIRED):
+    kv is [rows][Hkv][2][d] (token-major) or [Hkv][rows][2][d] (head-major),
+    contiguous; returns the two [..][..][d] views to pass as k / v."""
+    _need(kv, "kv", torch.bfloat16, 4)
+    if kv.shape[2] != 2:
+        raise ValueError("a paired cache buffer has shape [..][..][2][d]")
+    return kv[:, :, 0, :], kv[:, :, 1, :]
+
+
+def _need_kv(k, v, names, flags):
+    """Prefix or cache tensors: contiguous 3-D bf16 tensors, or with
+    SIMSD_KV_PAIRED the two halves of one contiguous [..][..][2][d] buffer
+    (see kv_pair_views)."""
+    if not flags & SIMSD_KV_PAIRED:
+        _need(k, names[0], torch.bfloat16, 3)
+        _need(v, names[1], torch.bfloat16, 3)
+        return
+    for t, n in ((k, names[0]), (v, names[1])):
+        if not torch.is_tensor(t) or t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3:
+            raise ValueError(f"{n} must be a 3-dim bf16 device tensor")
+    d = k.shape[2]
+    want = (k.shape[1] * 2 * d, 2 * d, 1)
+    if (tuple(k.stride()) != want or tuple(v.stride()) != want or v.shape != k.shape
+            or v.data_ptr() != k.data_ptr() + 2 * d):
+        raise ValueError(f"with SIMSD_KV_PAIRED, {names[0]} / {names[1]} must be the halves of one "
+                         "contiguous [..][..][2][d] buffer (kv_pair_views)")
+
+
 def _need(t, name, dtype, dims=None, device=True):
     if not torch.is_tensor(t):
         raise TypeError(f"{name} must be a tensor")
@@ -186,7 +215,8 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
                            flags: int = 0, status=None, workspace=None, stream=None):
     """Verify attention. Returns out ([b][2B][Hq][d], bf16 or fp32 with SIMSD_OUT_F32).
 
-    k_pre / v_pre are [sum P][Hkv][d], or [Hkv][sum P][d] with SIMSD_KV_HEAD_MAJOR.
+    k_pre / v_pre are [sum P][Hkv][d], or [Hkv][sum P][d] with SIMSD_KV_HEAD_MAJOR;
+    with SIMSD_KV_PAIRED the two halves of one [..][..][2][d] buffer (kv_pair_views).
 
     max_prefix: host int >= every prefix length; if None it is read back from
     prefix_offsets (a device-to-host copy, so not for timed loops).
@@ -218,8 +248,7 @@ def _attention(fn, q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, 
                scale, flags, status, workspace, stream, rope):
     for t, n in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk")):
         _need(t, n, torch.bfloat16, 4)
-    for t, n in ((k_pre, "k_pre"), (v_pre, "v_pre")):
-        _need(t, n, torch.bfloat16, 3)
+    _need_kv(k_pre, v_pre, ("k_pre", "v_pre"), flags)
     _need(prefix_offsets, "prefix_offsets", torch.int32, 1)
     _need(tau, "tau", torch.int32, 2)
     b, twoB, Hq, d = q_blk.shape
@@ -272,8 +301,7 @@ def simsd_verify_attention_mask(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offset
     word c // 64 of row r: row r sees block key c). Returns out."""
     for t, n in ((q_blk, "q_blk"), (k_blk, "k_blk"), (v_blk, "v_blk")):
         _need(t, n, torch.bfloat16, 4)
-    for t, n in ((k_pre, "k_pre"), (v_pre, "v_pre")):
-        _need(t, n, torch.bfloat16, 3)
+    _need_kv(k_pre, v_pre, ("k_pre", "v_pre"), flags)
     _need(prefix_offsets, "prefix_offsets", torch.int32, 1)
     _need(block_mask, "block_mask", torch.int64, 3)
     b, R, Hq, d = q_blk.shape
@@ -391,8 +419,7 @@ def simsd_commit_kv(k_blk, v_blk, tau, accept_len, k_cache, v_cache, cache_offse
     cache_offsets_with_lens)."""
     for t, n in ((k_blk, "k_blk"), (v_blk, "v_blk")):
         _need(t, n, torch.bfloat16, 4)
-    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, n, torch.bfloat16, 3)
+    _need_kv(k_cache, v_cache, ("k_cache", "v_cache"), flags)
     _need(tau, "tau", torch.int32, 2)
     _need(accept_len, "accept_len", torch.int32, 1)
     _need(cache_offsets, "cache_offsets", torch.int32, 1)

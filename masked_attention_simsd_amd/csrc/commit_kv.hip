@@ -70,10 +70,14 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
     const int h = c / per_head, piece = c % per_head;
     const uint16_t* src = (tensor ? a.v_blk : a.k_blk) +
                           (static_cast<size_t>(s) * 2 * B * a.Hkv + h) * a.d + piece * 8;
-    // cache row `row` of head h: token-major (row Hkv + h) d, head-major (h C + row) d
-    const size_t rstride = a.head_major ? static_cast<size_t>(a.d) : static_cast<size_t>(a.Hkv) * a.d;
+    // cache row `row` of head h: token-major (row Hkv + h) d, head-major (h C + row) d,
+    // both times 2 with the paired layout (key and value rows adjacent)
+    const size_t rstride = static_cast<size_t>(a.pair) *
+                           (a.head_major ? static_cast<size_t>(a.d) : static_cast<size_t>(a.Hkv) * a.d);
     uint16_t* dst = (tensor ? a.v_cache : a.k_cache) +
-                    (a.head_major ? static_cast<size_t>(h) * C * a.d : static_cast<size_t>(h) * a.d) + piece * 8;
+                    static_cast<size_t>(a.pair) *
+                        (a.head_major ? static_cast<size_t>(h) * C * a.d : static_cast<size_t>(h) * a.d) +
+                    piece * 8;
     for (int t0 = 0; t0 < L; t0 += kRowsInFlight) {
       // Slots past L repeat the last accepted row: they load it and store the
       // same bytes to its own place again (same thread, same value), so both

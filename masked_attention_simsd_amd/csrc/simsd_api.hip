@@ -16,6 +16,13 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The paired K/V layout needs the value half to start d elements after the
+// key half of the same buffer (no prefix pointers: nothing to check).
+bool paired_ok(uint32_t flags, const void* k, const void* v, int d) {
+  if (!(flags & SIMSD_KV_PAIRED) || !k || !v) return true;
+  return reinterpret_cast<uintptr_t>(v) == reinterpret_cast<uintptr_t>(k) + static_cast<uintptr_t>(d) * 2u;
+}
+
 int launch_status(hipError_t e) {
   if (e == hipSuccess) return SIMSD_OK;
   g_last_hip_error = static_cast<int>(e);
@@ -55,8 +62,9 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
   if (rc) return rc;
   if (max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return SIMSD_ERR_SIZE;
   const uint32_t rule = flags & 3u;
-  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS)))
+  if (rule == 3u || (flags & ~(3u | SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS | SIMSD_KV_PAIRED)))
     return SIMSD_ERR_FLAGS;
+  if (!paired_ok(flags, k_pre, v_pre, d)) return SIMSD_ERR_FLAGS;
   if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)))
@@ -114,6 +122,7 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
   a.data_rule = static_cast<int>(rule);
   a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
   a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  a.kv_pair = (flags & SIMSD_KV_PAIRED) ? 2 : 1;
   const bool lens = (flags & SIMSD_PREFIX_LENS) != 0;
   a.prefix_lens = lens ? prefix_offsets + b + 1 : prefix_offsets + 1;
   a.prefix_lens_are_ends = lens ? 0 : 1;
@@ -203,7 +212,8 @@ int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void
   int rc = check_common(b, 1, Hq, Hkv, d);
   if (rc) return rc;
   if (max_prefix < 0 || max_prefix > simsd::kMaxPrefix) return SIMSD_ERR_SIZE;
-  if (flags & ~(SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS)) return SIMSD_ERR_FLAGS;
+  if (flags & ~(SIMSD_OUT_F32 | SIMSD_KV_HEAD_MAJOR | SIMSD_PREFIX_LENS | SIMSD_KV_PAIRED)) return SIMSD_ERR_FLAGS;
+  if (!paired_ok(flags, k_pre, v_pre, d)) return SIMSD_ERR_FLAGS;
   if (!std::isfinite(scale)) return SIMSD_ERR_SCALE;
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(out) ||
       (k_pre && !aligned16(k_pre)) || (v_pre && !aligned16(v_pre)) ||
@@ -247,6 +257,7 @@ int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void
   a.data_rule = 0;
   a.out_f32 = (flags & SIMSD_OUT_F32) ? 1 : 0;
   a.kv_head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  a.kv_pair = (flags & SIMSD_KV_PAIRED) ? 2 : 1;
   const bool lens = (flags & SIMSD_PREFIX_LENS) != 0;
   a.prefix_lens = lens ? prefix_offsets + b + 1 : prefix_offsets + 1;
   a.prefix_lens_are_ends = lens ? 0 : 1;
@@ -342,7 +353,8 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
     return SIMSD_ERR_NULL;
   int rc = check_common(b, B, Hkv, Hkv, d);
   if (rc) return rc;
-  if (flags & ~SIMSD_KV_HEAD_MAJOR) return SIMSD_ERR_FLAGS;
+  if (flags & ~(SIMSD_KV_HEAD_MAJOR | SIMSD_KV_PAIRED)) return SIMSD_ERR_FLAGS;
+  if (!paired_ok(flags, k_cache, v_cache, d)) return SIMSD_ERR_FLAGS;
   if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
     return SIMSD_ERR_ALIGN;
   // each workgroup rewrites its sequence's length after reading its inputs:
@@ -368,6 +380,7 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
   a.status = status;
   a.b = b, a.B = B, a.Hkv = Hkv, a.d = d;
   a.head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;
+  a.pair = (flags & SIMSD_KV_PAIRED) ? 2 : 1;
   return launch_status(simsd::launch_commit_kv(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -102,6 +102,7 @@ struct AttnArgs {
   int xcd_remap;      // 1: workgroup ids remapped so a unit's splits share an XCD
   int rotate;         // 1: each unit starts its prefix walk at its own tile
   int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
+  int kv_pair;        // 2 with the paired layout (key and value rows adjacent), else 1
   // RoPE-copy fused into the prologue (rope != 0): query rows and block key
   // rows are rotated on the fly; the rotated block keys go to k_rot if set
   int rope;
@@ -134,6 +135,7 @@ struct CommitArgs {
   int32_t* status;
   int b, B, Hkv, d;
   int head_major;
+  int pair;  // 2 with the paired layout (key and value rows adjacent), else 1
 };
 
 struct AttnPlan {

@@ -377,10 +377,14 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   const int key_hi = split == ns - 1 ? P : (split + 1) * a.chunk - a.shift;
 
   // ---- tile schedule: (split 0) the block tiles, then the prefix tiles of this chunk ----
-  // prefix rows of (s, g): token-major [sum P][Hkv][d] or head-major [Hkv][sum P][d]
-  const uint32_t rsb = a.kv_head_major ? ROW_B : static_cast<uint32_t>(a.Hkv) * ROW_B;  // bytes between rows
-  const size_t pre0 = a.kv_head_major ? (static_cast<size_t>(g) * rows_total + o0) * D
-                                      : (static_cast<size_t>(o0) * a.Hkv + g) * D;
+  // prefix rows of (s, g): token-major [sum P][Hkv][d] or head-major [Hkv][sum P][d];
+  // with the paired layout every (token, head) slot holds the key row then
+  // the value row ([..][2][d]), so rows are kv_pair times as far apart
+  const uint32_t rsb = static_cast<uint32_t>(a.kv_pair) *
+                       (a.kv_head_major ? ROW_B : static_cast<uint32_t>(a.Hkv) * ROW_B);  // bytes between rows
+  const size_t pre0 = static_cast<size_t>(a.kv_pair) *
+                      (a.kv_head_major ? (static_cast<size_t>(g) * rows_total + o0) * D
+                                       : (static_cast<size_t>(o0) * a.Hkv + g) * D);
   const char* kpre = reinterpret_cast<const char*>(a.k_pre + pre0);
   const char* vpre = reinterpret_cast<const char*>(a.v_pre + pre0);
   const uint32_t rsb_blk = static_cast<uint32_t>(a.Hkv) * ROW_B;  // block rows are [2B][Hkv][d]

@@ -64,7 +64,10 @@ def test_attention_host_errors(lib):
     assert _attn(lib, Hq=6, Hkv=4) == 3
     assert _attn(lib, d=96) == 4
     assert _attn(lib, flags=3) == 5
-    assert _attn(lib, flags=32) == 5
+    assert _attn(lib, flags=64) == 5
+    # the paired K/V layout needs v_pre == k_pre + d elements
+    assert _attn(lib, flags=binding.SIMSD_KV_PAIRED) == 5
+    assert _attn(lib, flags=binding.SIMSD_KV_PAIRED, vp=ctypes.c_void_p(FAKE.value + 2 * 128), ws=None) == 6
     assert _attn(lib, scale=float("nan")) == 9
     assert _attn(lib, out=MISALIGNED) == 7
     assert _attn(lib, ws=None) == 6
