@@ -128,6 +128,7 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
   a.prefix_lens_are_ends = lens ? 0 : 1;
   a.xcd_remap = plan.xcd_remap;
   a.rotate = plan.rotate;
+  a.lpt = plan.lpt;
   if (rope) {
     a.rope = 1;
     a.start_pos = rope->start_pos;
@@ -263,6 +264,7 @@ int simsd_verify_attention_mask(const void* q_blk, const void* k_blk, const void
   a.prefix_lens_are_ends = lens ? 0 : 1;
   a.xcd_remap = plan.xcd_remap;
   a.rotate = plan.rotate;
+  a.lpt = plan.lpt;
   a.mask_mode = 1;
   a.block_mask = block_mask;
   a.mask_words = (R + 63) / 64;

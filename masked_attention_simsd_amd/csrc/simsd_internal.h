@@ -101,6 +101,7 @@ struct AttnArgs {
   int out_f32;
   int xcd_remap;      // 1: workgroup ids remapped so a unit's splits share an XCD
   int rotate;         // 1: each unit starts its prefix walk at its own tile
+  int lpt;            // 1: unsplit launch, workgroups dispatched first take the longest sequences
   int kv_head_major;  // prefix cache layout: 0 [sum P][Hkv][d], 1 [Hkv][sum P][d]
   int kv_pair;        // 2 with the paired layout (key and value rows adjacent), else 1
   // RoPE-copy fused into the prologue (rope != 0): query rows and block key
@@ -143,6 +144,7 @@ struct AttnPlan {
   int pipe;           // key-tile pipeline variant (keys per tile x ring stages)
   int xcd_remap;
   int rotate;
+  int lpt;
   int rows_per_wg;
   int row_slices;
   int chunk, nsplit, shift;

@@ -272,13 +272,37 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 
   // ---- which (sequence, KV head, row slice, split) this workgroup owns ----
   const int wg = blockIdx.x;
-  const int logical = a.xcd_remap ? (wg & 7) * (a.total_grid >> 3) + (wg >> 3) : wg;
+  const int logical = a.lpt ? wg : (a.xcd_remap ? (wg & 7) * (a.total_grid >> 3) + (wg >> 3) : wg);
   if (logical >= a.total_real) return;
   const int split = logical % a.nsplit;
   const int us = logical / a.nsplit;
   const int slice = us % a.row_slices;
   const int unit = us / a.row_slices;
-  const int s = unit / a.Hkv, g = unit % a.Hkv;
+  int s = unit / a.Hkv;
+  const int g = unit % a.Hkv;
+  if (a.lpt) {
+    // Longest first (unsplit launches of at most 64 sequences whose
+    // workgroups do not all fit at once): workgroups are dispatched in id
+    // order, so the k-th group of Hkv ids takes the k-th longest sequence and
+    // the short ones fill the CUs that free up at the end. Wave 0 ranks the
+    // sequences by prefix length (ties by index), identically in every
+    // workgroup, and picks the one of rank s.
+    __shared__ int lpt_seq;
+    if (wave == 0) {
+      const int sl = lane < a.b ? lane : 0;
+      int pl = a.prefix_lens[sl] - (a.prefix_lens_are_ends ? a.offsets[sl] : 0);
+      pl = lane < a.b ? max(pl, 0) : -1;
+      int rank = 0;
+      for (int t = 0; t < kWave; ++t) {
+        const int pt = __shfl(pl, t, kWave);
+        rank += (pt > pl || (pt == pl && t < lane)) ? 1 : 0;
+      }
+      const unsigned long long hit = __ballot(lane < a.b && rank == s);
+      if (lane == 0) lpt_seq = __ffsll(static_cast<long long>(hit)) - 1;
+    }
+    __syncthreads();
+    s = lpt_seq;
+  }
   // block keys: the 2B rows of the paired block, or the R rows of an
   // explicit-mask call (no tau, B = 0)
   const int B = a.B, twoB = MASK ? a.nblk : 2 * a.B;
@@ -1032,6 +1056,12 @@ hipError_t launch_d_default(const AttnArgs& a, const AttnPlan& p, hipStream_t st
     return launch_variant<D, 4, 2, 64, 2, 4, 1, MODE>(a, stream);
   }
   if constexpr (D == 128) {
+    if (p.pipe == 6) {
+      // the longest-first ring of large ragged batches, if the RoPE table fits beside it
+      const size_t dyn = MODE == kModeTauRope ? rope_table_bytes(a) : 0;
+      if (lds_fits<D, 4, 1, 64, 4, 4, 1, MODE>(dyn)) return launch_variant<D, 4, 1, 64, 4, 4, 1, MODE>(a, stream);
+      return launch_variant<D, 4, 1, 64, 2, 4, 1, MODE>(a, stream);
+    }
     if (p.pipe != 1) return launch_variant<D, 4, 1, 32, 4, 4, 1, MODE>(a, stream);
   }
   return launch_variant<D, 4, 1, 64, 2, 4, 1, MODE>(a, stream);
@@ -1140,11 +1170,24 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
   // the other's softmax, and with 128-key tiles, which halve the barriers per
   // byte (b16, interleaved runs: 110.5 us vs 114.1 with 64-key tiles and
   // 116-119 with one wave per row group).
+  // An unsplit launch of more than 256 workgroups (a large ragged batch) is
+  // ended by its longest sequences, each streamed by one workgroup. With 64
+  // rows, d = 128 and at most 64 sequences it runs longest first (ids in
+  // descending order of prefix length) on a 64 x 4 ring that keeps one
+  // workgroup per CU with three tiles in flight: the long sequences start
+  // first at the higher per-workgroup rate and the short ones fill the CUs
+  // as they free up (ragged, 64 x U[512, 8192]: 222-224 us against 240.5 us
+  // for all 512 workgroups resident two per CU on the 64 x 2 ring; without
+  // the order the 64 x 4 ring takes 289 us).
   const long wgs = units * nsplit;
-  const int pipe_default = p.qb == 1 ? (wgs > 256 ? 1 : 0) : (wgs <= 256 ? 9 : 0);
+  const bool lpt_ok = nsplit == 1 && p.row_slices == 1 && b <= 64;
+  const bool lpt_ring = p.qb == 1 && wgs > 256 && lpt_ok && d == 128;
+  const int pipe_default = p.qb == 1 ? (wgs > 256 ? (lpt_ring ? 6 : 1) : 0) : (wgs <= 256 ? 9 : 0);
   p.pipe = env_int("SIMSD_ATTN_PIPE", pipe_default);
   p.chunk = chunk;
   p.nsplit = nsplit;
+  // tuning: SIMSD_ATTN_LPT = 0 / 1 forces the longest-first order off / on
+  p.lpt = (env_int("SIMSD_ATTN_LPT", lpt_ring ? 1 : 0) != 0 && lpt_ok) ? 1 : 0;
   // tuning: prefix keys moved off split 0, which also takes the block tiles
   // (SIMSD_ATTN_SHIFT; measured neutral on MI355X, so 0 by default)
   p.shift = std::max(0, std::min(chunk / 2, env_int("SIMSD_ATTN_SHIFT", 0)));
