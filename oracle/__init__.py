@@ -58,21 +58,32 @@ BAD_TAU, COMMIT_OVERFLOW = 1, 64
 _lib = None
 
 
+def compile_source(src: str, out: str) -> None:
+    """gcc -O2, no fast-math, no FMA contraction: the one way the oracle is built."""
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-fno-fast-math", src, "-o", out, "-lm"])
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    """Compile the oracle (only when the source is newer than the library)."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-                               "-fno-fast-math", SRC, "-o", tmp, "-lm"])
+        compile_source(SRC, tmp)
         os.replace(tmp, LIB)
     return LIB
+
+
+# The test of the pins themselves (tests/test_oracle_mutants.py) runs the pin
+# tests against copies of the oracle with one planted mistake each; such a copy
+# is loaded from the path in this variable instead of the library built here.
+MUTANT_ENV = "SIMSD_ORACLE_MUTANT_LIB"
 
 
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(LIB)
+        path = os.environ.get(MUTANT_ENV) or build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         D = ctypes.c_double
