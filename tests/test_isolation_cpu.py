@@ -1,0 +1,52 @@
+"""The product path and the oracle stay apart, and the product path has no
+fallback: the HIP library's sources and its binding never name the oracle,
+the oracle never names the HIP path, importing the binding loads no oracle
+module, and a missing library is an error rather than a silent substitute."""
+import glob
+import os
+import subprocess
+import sys
+
+import pytest
+
+from masked_attention_simsd_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _sources(*patterns):
+    out = []
+    for p in patterns:
+        out += glob.glob(os.path.join(ROOT, p), recursive=True)
+    assert out, patterns
+    return out
+
+
+def test_product_sources_never_name_the_oracle():
+    files = _sources("masked_attention_simsd_amd/**/*.py", "masked_attention_simsd_amd/csrc/*.hip",
+                     "masked_attention_simsd_amd/csrc/*.h", "include/*.h")
+    for f in files:
+        text = open(f).read()
+        for word in ("import oracle", "from oracle", "simsd_oracle", "oracle/"):
+            assert word not in text, f"{os.path.relpath(f, ROOT)} names the oracle ({word!r})"
+
+
+def test_oracle_never_names_the_hip_path():
+    for f in _sources("oracle/*.py", "oracle/*.c"):
+        text = open(f).read()
+        for word in ("masked_attention_simsd_amd", "simsd_internal", "libsimsd.so", "include/simsd.h",
+                     "#include \"simsd"):
+            assert word not in text, f"{os.path.relpath(f, ROOT)} names the HIP path ({word!r})"
+
+
+def test_importing_the_binding_loads_no_oracle():
+    code = "import sys, masked_attention_simsd_amd.binding, masked_attention_simsd_amd.synth; " \
+           "sys.exit(1 if any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules) else 0)"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-500:]
+
+
+def test_missing_library_is_an_error(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library(str(tmp_path / "libsimsd.so"))
