@@ -74,6 +74,7 @@ SHAPES = [
     (1, 32, 8, 128, 16, (2049, 2049)),
     (1, 4, 1, 64, 64, (130, 130)),
     (4, 32, 4, 128, 5, (1, 3000)),
+    (2, 32, 8, 128, 64, (100, 1500)),  # the largest block (B = 64): 512 rows per KV head in 4 slices
 ]
 
 
