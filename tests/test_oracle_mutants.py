@@ -7,6 +7,7 @@ way the oracle is, and the oracle's pin tests are run against it in a child
 process (the oracle loads the mutant through its MUTANT_ENV hook): at least
 one pin must fail for every mutant, and none for an unaltered copy. Nothing
 here touches a GPU or the HIP library."""
+import json
 import os
 import subprocess
 import sys
@@ -71,6 +72,37 @@ MUTANTS = {
 }
 
 
+# Mutants of the Python-side row movement (commit_kv, pack_regions): the child
+# re-executes the oracle module's source with the edit applied, in place, before
+# running the pins.
+PY_MUTANTS = {
+    "commit_in_position_order": [("k = int(inv[step])", "k = step")],
+    "commit_mask_slot_rows": [("kc[:, row] = kb[s, k]\n", "kc[:, row] = kb[s, k + B]\n"),
+                              ("kc[row] = kb[s, k]\n", "kc[row] = kb[s, k + B]\n"),
+                              ("vc[:, row] = vb[s, k]\n", "vc[:, row] = vb[s, k + B]\n"),
+                              ("vc[row] = vb[s, k]\n", "vc[row] = vb[s, k + B]\n")],
+    "commit_row_off_by_one": [("row = int(off[s]) + int(ln[s]) + step", "row = int(off[s]) + int(ln[s]) + step + 1")],
+    "commit_length_kept": [("ln[s] += L", "ln[s] += 0")],
+    "commit_overflow_off_by_one": [("int(ln[s]) + L > cap", "int(ln[s]) + L > cap + 1")],
+    "commit_values_from_keys": [("vc[:, row] = vb[s, k]", "vc[:, row] = kb[s, k]"),
+                                ("vc[row] = vb[s, k]", "vc[row] = kb[s, k]")],
+    "pack_whole_regions": [("np.arange(off[s], off[s] + ln[s])", "np.arange(off[s], off[s + 1])")],
+    "pack_offsets_of_regions": [("po[1:] = np.cumsum(ln)", "po[1:] = np.cumsum(np.diff(off))")],
+}
+
+_PY_CHILD = """
+import json, os, sys
+import oracle
+src = open(oracle.__file__).read()
+for old, new in json.loads(os.environ["ORACLE_PY_EDITS"]):
+    assert src.count(old) == 1, old
+    src = src.replace(old, new)
+exec(compile(src, oracle.__file__, "exec"), oracle.__dict__)
+import pytest
+sys.exit(pytest.main(sys.argv[1:]))
+"""
+
+
 def _mutate(src: str, edits) -> str:
     for old, new in edits:
         assert src.count(old) == 1, f"mutation anchor not unique or missing: {old!r}"
@@ -78,10 +110,15 @@ def _mutate(src: str, edits) -> str:
     return src
 
 
-def _run_pins(lib_path: str):
+def _run_pins(lib_path: str, py_edits=None):
     env = dict(os.environ)
     env[oracle.MUTANT_ENV] = lib_path
-    cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider", *PIN_FILES]
+    args = ["-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider", *PIN_FILES]
+    if py_edits:
+        env["ORACLE_PY_EDITS"] = json.dumps(py_edits)
+        cmd = [sys.executable, "-c", _PY_CHILD, *args]
+    else:
+        cmd = [sys.executable, "-m", "pytest", *args]
     r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     lines = r.stdout.strip().splitlines()
     return r.returncode, lines[-1] if lines else r.stderr[-300:]
@@ -100,6 +137,7 @@ def outcomes(tmp_path_factory):
         libs[name] = lib
     with ThreadPoolExecutor(max_workers=4) as ex:
         futs = {name: ex.submit(_run_pins, lib) for name, lib in libs.items()}
+        futs.update({name: ex.submit(_run_pins, libs["unaltered"], edits) for name, edits in PY_MUTANTS.items()})
         return {name: f.result() for name, f in futs.items()}
 
 
@@ -108,7 +146,7 @@ def test_unaltered_copy_passes_every_pin(outcomes):
     assert rc == 0, summary
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(PY_MUTANTS))
 def test_pins_catch_mutant(outcomes, name):
     rc, summary = outcomes[name]
     # a pin must fail (an assertion, reported by pytest), not the process crash
