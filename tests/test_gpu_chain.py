@@ -12,17 +12,24 @@ from gpu_util import ORACLE_THREADS, bf16_round, f64, inputs, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg", ["tiny", "b4", "b8"])
-def test_chain_matches_oracle(cfg):
-    say(f"chain {cfg}")
+@pytest.mark.parametrize("cfg,paired", [("tiny", False), ("b4", False), ("b8", False), ("b8", True)],
+                         ids=["tiny", "b4", "b8", "b8_paired_head_major"])
+def test_chain_matches_oracle(cfg, paired):
+    say(f"chain {cfg} paired head-major {paired}")
     x = inputs(cfg)
     w = x["workload"]
     g = to_dev(x)
+    flags = 0
+    if paired:
+        # the cache layout the benchmark times: [Hkv][sum P][2][d]
+        kv = torch.stack([g["k_pre"].transpose(0, 1), g["v_pre"].transpose(0, 1)], dim=2).contiguous()
+        g["k_pre"], g["v_pre"] = binding.kv_pair_views(kv)
+        flags = binding.SIMSD_KV_HEAD_MAJOR | binding.SIMSD_KV_PAIRED
     status = torch.zeros(w.b, dtype=torch.int32, device="cuda")
     binding.simsd_rope_copy(g["q_blk"], g["k_blk"], g["start_pos"], w.rope_base)
     out = binding.simsd_verify_attention(g["q_blk"], g["k_blk"], g["v_blk"], g["k_pre"], g["v_pre"],
                                          g["prefix_offsets"], g["tau"], max_prefix=w.prefix[1],
-                                         status=status)
+                                         flags=flags, status=status)
     L, corr = binding.simsd_accept(g["p"], g["q"], g["draft"], g["tau"], g["u"], status=status)
     torch.cuda.synchronize()
 

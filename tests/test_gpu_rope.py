@@ -22,7 +22,7 @@ def _check(gpu, ref_f64, what):
     assert exact >= 0.9999, what
 
 
-@pytest.mark.parametrize("cfg", ["tiny", "b4", "b8", "b16"])
+@pytest.mark.parametrize("cfg", ["tiny", "b4", "b8", "b16", "ragged"])
 @pytest.mark.parametrize("flags", [0, binding.SIMSD_ROPE_INTERLEAVED, binding.SIMSD_ROPE_NO_COPY])
 def test_rope_copy_matches_oracle(cfg, flags):
     say(f"rope {cfg} flags={flags}")
