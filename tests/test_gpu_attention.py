@@ -218,3 +218,23 @@ def test_one_workspace_shared_by_calls_of_different_shapes():
             err = float(np.abs(f64(out) - refs[i]).max())
             assert err <= TOL_F32, (rnd, i, err)
     assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("b,prefix,layout", [
+    (40, (16, 3000), binding.SIMSD_KV_HEAD_MAJOR | binding.SIMSD_KV_PAIRED),  # > 256 units, longest first
+    (72, (16, 600), binding.SIMSD_KV_HEAD_MAJOR),                             # > 64 sequences: two per CU
+    (72, (0, 900), 0),
+], ids=["lpt_b40", "b72_head_major", "b72_token_major"])
+def test_large_batch_schedules_match_oracle(b, prefix, layout):
+    """Unsplit launches of more than 256 workgroups: the longest-first order
+    (at most 64 sequences) and the plain order beyond 64 sequences, checked on
+    a sample of sequences that includes the longest and the shortest."""
+    say(f"large batch b={b} prefix={prefix} layout={layout}")
+    w = synth.custom(b=b, Hq=32, Hkv=8, d=128, B=8, prefix=prefix)
+    x = synth.make_inputs(w, with_accept=False, seed=31 + b)
+    out, lse = run_gpu(x, flags=layout)
+    lens = (x["prefix_offsets"][1:] - x["prefix_offsets"][:-1]).tolist()
+    seqs = sorted({0, 1, b // 2, b - 1, int(np.argmin(lens)), int(np.argmax(lens))})
+    ref, ref_lse = run_oracle(subset_sequences(x, seqs))
+    idx = torch.tensor(seqs, device="cuda")
+    compare(out[idx], lse[idx], ref, ref_lse, 0, TOL_BF16, f"b={b} seqs {seqs}")
