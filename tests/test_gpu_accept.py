@@ -114,3 +114,11 @@ def test_edge_cases():
     one = np.ones((4, 3, 1), np.float32)
     check(one, one, np.zeros((4, 3), np.int32), np.tile(np.array([[2, 3, 1]], np.int32), (4, 1)),
           rng.random((4, 4)).astype(np.float32), "V=1")
+    # a block of one position (B = 1): one ratio, then the correction from that row
+    p1 = rng.random((6, 1, 37)).astype(np.float32)
+    p1 /= p1.sum(-1, keepdims=True)
+    q1 = rng.random((6, 1, 37)).astype(np.float32)
+    q1 /= q1.sum(-1, keepdims=True)
+    u1 = rng.random((6, 2)).astype(np.float32)
+    u1[:3, 0] = 0.9999  # rejected: the correction is drawn
+    check(p1, q1, rng.integers(0, 37, (6, 1)).astype(np.int32), np.ones((6, 1), np.int32), u1, "B=1")
