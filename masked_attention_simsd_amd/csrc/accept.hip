@@ -42,6 +42,15 @@ constexpr int kMaxSegments = kMaxAcceptVocab / (kAccThreads * kMinPer);
 constexpr unsigned long long kReady = 1ull << 63;
 constexpr int kPollLimit = 1 << 16;  // bound on the polls of one mass word
 
+// Arrival counters of different sequences sit 128 bytes apart (their own
+// cache lines, as far as the fixed counter region allows): every workgroup of
+// a launch bumps one, and counters sharing a line serialise each other's
+// atomics.
+__device__ __forceinline__ int* seq_counter(const AcceptArgs& a, int s) {
+  const int stride = min(32, kMaxSeqCounters / a.b);
+  return a.counters + static_cast<size_t>(s) * stride;
+}
+
 // exp(x) for x <= 0 in fp64, relative error below 1e-14: Cody-Waite
 // reduction x = n ln2 + r with the two-part ln 2 of fdlibm (|r| <= ln2 / 2),
 // the Taylor series of e^r to degree 11 (truncation < 7e-15 there), and an
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   if (tid == 0) {
     __hip_atomic_store(words + seg, static_cast<unsigned long long>(__double_as_longlong(mine)) | kReady,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int prev = __hip_atomic_fetch_add(&a.counters[s], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int prev = __hip_atomic_fetch_add(seq_counter(a, s), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_last = prev == nseg - 1;
   }
   __syncthreads();
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     a.accept_len[s] = L;
     a.correction[s] = sh_pick;
     if (a.status && sh_stat) atomicOr(&a.status[s], sh_stat);
-    __hip_atomic_store(&a.counters[s], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(seq_counter(a, s), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
