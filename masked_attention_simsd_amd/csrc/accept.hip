@@ -50,6 +50,12 @@ __device__ __forceinline__ int* seq_counter(const AcceptArgs& a, int s) {
   const int stride = min(32, kMaxSeqCounters / a.b);
   return a.counters + static_cast<size_t>(s) * stride;
 }
+// The row-statistics counters (2 b B rows) likewise, 128 bytes apart for up to
+// 2048 rows; the workspace size reserves the padded region by the same rule.
+__device__ __forceinline__ int* row_counter(const AcceptArgs& a, int row) {
+  const int rows = 2 * a.b * a.B;
+  return a.row_counters + static_cast<size_t>(row) * (rows <= 2048 ? 32 : 1);
+}
 
 // exp(x) for x <= 0 in fp64, relative error below 1e-14: Cody-Waite
 // reduction x = n ln2 + r with the two-part ln 2 of fdlibm (|r| <= ln2 / 2),
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
     __hip_atomic_store(words + 2 * seg + 1,
                        static_cast<unsigned long long>(__double_as_longlong(sum)) | kReady, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    const int prev = __hip_atomic_fetch_add(&a.row_counters[row], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int prev = __hip_atomic_fetch_add(row_counter(a, row), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_last = prev == a.nseg1 - 1;
   }
   __syncthreads();
@@ -555,7 +561,7 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
   if (tid == 0) {
     a.row_stats[2 * static_cast<size_t>(row)] = static_cast<double>(M);
     a.row_stats[2 * static_cast<size_t>(row) + 1] = 1.0 / S;
-    __hip_atomic_store(&a.row_counters[row], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(row_counter(a, row), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -307,7 +307,10 @@ size_t simsd_accept_logits_workspace(int b, int B, int V) {
   const long nseg1 = (V + simsd::kRowStatSeg - 1) / simsd::kRowStatSeg;
   if (rows * nseg1 > simsd::kMaxRowStatUnits) return 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return base + up(rows * sizeof(int32_t)) + up(rows * nseg1 * 2 * sizeof(uint64_t)) +
+  // row counters 128 bytes apart for up to 2048 rows (the row-statistics
+  // kernel indexes them with the same rule), packed beyond that
+  const long row_stride = rows <= 2048 ? 32 : 1;
+  return base + up(rows * row_stride * sizeof(int32_t)) + up(rows * nseg1 * 2 * sizeof(uint64_t)) +
          up(rows * 2 * sizeof(double));
 }
 
@@ -339,7 +342,7 @@ int simsd_accept_logits(const float* target_logits, const float* draft_logits, f
   a.seg_sum = reinterpret_cast<double*>(ws + static_cast<size_t>(simsd::kMaxSeqCounters) * sizeof(int32_t));
   size_t off = acc_bytes;
   a.row_counters = reinterpret_cast<int32_t*>(ws + off);
-  off += up(rows * sizeof(int32_t));
+  off += up(rows * (rows <= 2048 ? 32 : 1) * sizeof(int32_t));  // padded as in the workspace size
   a.row_words = reinterpret_cast<unsigned long long*>(ws + off);
   off += up(rows * nseg1 * 2 * sizeof(uint64_t));
   a.row_stats = reinterpret_cast<double*>(ws + off);
