@@ -565,20 +565,18 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
   }
 }
 
-// Entries per thread (segment width / 256): 8 (2048-entry segments), 16 for
-// vocabularies of 64K entries and more, where fewer and longer segments mean
-// fewer masses for the last arrival to gather, and for batches whose
-// 2048-entry segments would give more than one workgroup per CU (measured on
-// one MI355X, back to back: b = 16, V = 32768, 4 / 8 / 16 -> 13.2 / 11.6 /
-// 12.1 us; b = 8, V = 151936 -> 22.6 / 17.0 / 15.5 us; b = 64, V = 32768 ->
-// 21.1 / 16.6 / 15.5 us). SIMSD_ACCEPT_PER = 4, 8 or 16 overrides it (read
-// on every call).
+// Entries per thread (segment width / 256): 4 (1024-entry segments). With
+// the arrival counters on their own cache lines, more and shorter segments
+// win at every measured shape (one MI355X, back to back, 4 / 8 / 16:
+// b = 16, V = 32768 -> 9.0 / 9.8 / 11.9 us; b = 64, V = 32768 -> 11.9 / 13.5 /
+// 15.1 us; b = 8, V = 151936 -> 11.4 / 12.5 / 14.1 us). SIMSD_ACCEPT_PER = 4,
+// 8 or 16 overrides it (read on every call).
 int accept_per(int b, int V) {
   const char* e = getenv("SIMSD_ACCEPT_PER");
   const int forced = e ? atoi(e) : 0;
   if (forced == 4 || forced == 8 || forced == 16) return forced;
-  const long wgs8 = static_cast<long>(b) * ((V + kAccThreads * 8 - 1) / (kAccThreads * 8));
-  return (V >= 65536 || wgs8 > 256) ? 16 : 8;
+  (void)b, (void)V;
+  return 4;
 }
 
 }  // namespace
