@@ -369,6 +369,37 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
                     void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens, int b,
                     int B, int Hkv, int d, uint32_t flags, int32_t* status, void* stream);
 
+/*
+ * simsd_set_tuning -- override one choice of the kernel plans, process-wide,
+ * for measurement and for tests that check every kernel variant against a
+ * reference. The plans read only these explicit settings (never the
+ * environment), so a call's plan and workspace size depend on its arguments
+ * and on the settings in force when it is made; change settings only while no
+ * call is being issued from another thread, and query workspace sizes after
+ * setting them. value -1 restores the plan's own choice for that key.
+ *   SIMSD_TUNE_ATTN_PIPE       attention key-tile ring / wave layout variant
+ *   SIMSD_TUNE_ATTN_TARGET_WG  workgroups the split plan aims for (>= 1)
+ *   SIMSD_TUNE_ATTN_CHUNK_MAX  cap on prefix keys per split (>= 64)
+ *   SIMSD_TUNE_ATTN_XCD_REMAP  0/1: keep a unit's splits on one XCD
+ *   SIMSD_TUNE_ATTN_ROTATE     0/1: per-unit starting prefix tile
+ *   SIMSD_TUNE_ATTN_LPT        0/1: longest-first order of unsplit launches
+ *   SIMSD_TUNE_ATTN_SHIFT      prefix keys moved off split 0 (>= 0)
+ *   SIMSD_TUNE_ACCEPT_PER      acceptance entries per thread: 4, 8 or 16
+ *   SIMSD_TUNE_ROWSTAT_PER     row-statistics entries per thread: 16, 32 or 64
+ * Returns SIMSD_OK, or SIMSD_ERR_SIZE for an unknown key or a value below -1.
+ */
+#define SIMSD_TUNE_ATTN_PIPE 0
+#define SIMSD_TUNE_ATTN_TARGET_WG 1
+#define SIMSD_TUNE_ATTN_CHUNK_MAX 2
+#define SIMSD_TUNE_ATTN_XCD_REMAP 3
+#define SIMSD_TUNE_ATTN_ROTATE 4
+#define SIMSD_TUNE_ATTN_LPT 5
+#define SIMSD_TUNE_ATTN_SHIFT 6
+#define SIMSD_TUNE_ACCEPT_PER 7
+#define SIMSD_TUNE_ROWSTAT_PER 8
+#define SIMSD_TUNE_COUNT 9
+int simsd_set_tuning(int key, int value);
+
 /* Static text for a simsd_status_t value. */
 const char* simsd_status_string(int code);
 

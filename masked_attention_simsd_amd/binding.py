@@ -25,13 +25,16 @@ SIMSD_KV_HEAD_MAJOR, SIMSD_PREFIX_LENS, SIMSD_KV_PAIRED = 8, 16, 32
 SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
 SIMSD_DEV_BAD_TOKEN, SIMSD_DEV_BAD_PREFIX, SIMSD_DEV_SYNC_TIMEOUT = 8, 16, 32
 SIMSD_DEV_COMMIT_OVERFLOW = 64
+# simsd_set_tuning keys
+TUNE_KEYS = {"attn_pipe": 0, "attn_target_wg": 1, "attn_chunk_max": 2, "attn_xcd_remap": 3,
+             "attn_rotate": 4, "attn_lpt": 5, "attn_shift": 6, "accept_per": 7, "rowstat_per": 8}
 
 EXPORTS = (
     "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_rope",
     "simsd_verify_attention_workspace", "simsd_verify_attention_mask",
     "simsd_verify_attention_mask_workspace",
     "simsd_accept", "simsd_accept_workspace", "simsd_accept_logits", "simsd_accept_logits_workspace",
-    "simsd_commit_kv", "simsd_status_string", "simsd_last_hip_error",
+    "simsd_commit_kv", "simsd_status_string", "simsd_last_hip_error", "simsd_set_tuning",
 )
 
 
@@ -82,6 +85,8 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_status_string.restype = ctypes.c_char_p
         lib.simsd_last_hip_error.argtypes = []
         lib.simsd_last_hip_error.restype = I
+        lib.simsd_set_tuning.argtypes = [I, I]
+        lib.simsd_set_tuning.restype = I
         _lib = lib
         return lib
 
@@ -93,6 +98,31 @@ def _check(fn: str, rc: int):
         if rc == 8:
             msg += f" (hipError {lib.simsd_last_hip_error()})"
         raise SimsdError(fn, rc, msg)
+
+
+def simsd_set_tuning(key, value: int):
+    """Override one kernel-plan choice process-wide (key: a name of TUNE_KEYS
+    or its number; value -1 restores the default)."""
+    k = TUNE_KEYS[key] if isinstance(key, str) else int(key)
+    _check("simsd_set_tuning", load_library().simsd_set_tuning(k, int(value)))
+
+
+class tuning:
+    """Context manager: tuning overrides for the calls made inside it, e.g.
+    ``with binding.tuning(attn_pipe=7): ...``; restores the defaults after."""
+
+    def __init__(self, **kw):
+        self.kw = kw
+
+    def __enter__(self):
+        for k, v in self.kw.items():
+            simsd_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k in self.kw:
+            simsd_set_tuning(k, -1)
+        return False
 
 
 def _ptr(t):

@@ -25,6 +25,7 @@
 //   scan over the segment masses, and rescans that segment with a
 //   workgroup-wide prefix sum for the first token whose running mass exceeds T.
 // Traffic: 2 V fp32 per rejecting sequence plus one segment re-read.
+#include "simsd.h"
 #include "simsd_internal.h"
 
 #include <stdlib.h>
@@ -569,11 +570,10 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
 // the arrival counters on their own cache lines, more and shorter segments
 // win at every measured shape (one MI355X, back to back, 4 / 8 / 16:
 // b = 16, V = 32768 -> 9.0 / 9.8 / 11.9 us; b = 64, V = 32768 -> 11.9 / 13.5 /
-// 15.1 us; b = 8, V = 151936 -> 11.4 / 12.5 / 14.1 us). SIMSD_ACCEPT_PER = 4,
-// 8 or 16 overrides it (read on every call).
+// 15.1 us; b = 8, V = 151936 -> 11.4 / 12.5 / 14.1 us). The tuning override
+// SIMSD_TUNE_ACCEPT_PER = 4, 8 or 16 replaces it.
 int accept_per(int b, int V) {
-  const char* e = getenv("SIMSD_ACCEPT_PER");
-  const int forced = e ? atoi(e) : 0;
+  const int forced = tuning(SIMSD_TUNE_ACCEPT_PER);
   if (forced == 4 || forced == 8 || forced == 16) return forced;
   (void)b, (void)V;
   return 4;
@@ -599,11 +599,10 @@ hipError_t launch_accept_mode(const AcceptArgs& a, hipStream_t stream) {
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) { return launch_accept_mode<false>(a, stream); }
 
-// Entries per thread of the row-statistics pass: SIMSD_ROWSTAT_PER = 16, 32
-// or 64 overrides the default (read on every call).
+// Entries per thread of the row-statistics pass: the tuning override
+// SIMSD_TUNE_ROWSTAT_PER = 16, 32 or 64 replaces the default.
 int row_stat_per() {
-  const char* e = getenv("SIMSD_ROWSTAT_PER");
-  const int forced = e ? atoi(e) : 0;
+  const int forced = tuning(SIMSD_TUNE_ROWSTAT_PER);
   return (forced == 16 || forced == 32 || forced == 64) ? forced : 32;
 }
 

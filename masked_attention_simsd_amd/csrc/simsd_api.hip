@@ -5,12 +5,16 @@
 // point allocates, frees or synchronises.
 #include "simsd.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
 #include "simsd_internal.h"
 
 namespace {
+
+// Tuning overrides (simsd_set_tuning); -1 = the plan's own choice.
+std::atomic<int> g_tuning[SIMSD_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
 
 thread_local int g_last_hip_error = 0;
 
@@ -142,7 +146,19 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
 
 }  // namespace
 
+namespace simsd {
+int tuning(int key) {
+  return key >= 0 && key < SIMSD_TUNE_COUNT ? g_tuning[key].load(std::memory_order_relaxed) : -1;
+}
+}  // namespace simsd
+
 extern "C" {
+
+int simsd_set_tuning(int key, int value) {
+  if (key < 0 || key >= SIMSD_TUNE_COUNT || value < -1) return SIMSD_ERR_SIZE;
+  g_tuning[key].store(value, std::memory_order_relaxed);
+  return SIMSD_OK;
+}
 
 int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, int B, int Hq,
                     int Hkv, int d, float rope_base, uint32_t flags, void* stream) {

@@ -184,6 +184,10 @@ constexpr int kMaxPrefix = 1 << 30; // largest max_prefix (key counts stay far f
 constexpr long kMaxRopeTableBytes = 64 * 1024;  // fused RoPE cos/sin table (LDS beside the key ring)
 constexpr int kAttnMaxUnits = kMaxSeqCounters;  // (sequence, KV head, row slice) units per call
 
+// Tuning overrides set through simsd_set_tuning (process-wide, default -1 =
+// the plan's own choice). Keys are the SIMSD_TUNE_* values of simsd.h.
+int tuning(int key);
+
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule);
 // the same for `nrows` computed query rows per sequence (explicit-mask calls)
 AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_prefix);

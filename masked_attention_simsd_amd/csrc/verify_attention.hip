@@ -35,10 +35,10 @@
 //    log-sum-exp rule, writes the output and resets the counter. Workgroup ids
 //    are remapped so the chunks of one unit run on the same XCD (ids are
 //    dispatched round-robin over the 8 XCDs).
+#include "simsd.h"
 #include "simsd_internal.h"
 
 #include <algorithm>
-#include <cstdlib>
 
 namespace simsd {
 
@@ -1106,10 +1106,10 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   return launch_variant<D, 4, 1, 64, 2>(a, stream);
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  return std::atoi(v);
+// A tuning override if one is set, else the plan's own value.
+int tuned(int key, int dflt) {
+  const int v = tuning(key);
+  return v < 0 ? dflt : v;
 }
 
 }  // namespace
@@ -1121,7 +1121,7 @@ int env_int(const char* name, int dflt) {
 // splits only as far as needed to give each of the 256 CUs a workgroup:
 // units >= 256 run unsplit (a ragged batch then has all its workgroups
 // resident at once, two per CU), fewer units get ceil(256 / units) splits.
-// Tuning overrides: SIMSD_ATTN_TARGET_WG, SIMSD_ATTN_CHUNK_MAX, SIMSD_ATTN_PIPE.
+// Tuning overrides (simsd_set_tuning): SIMSD_TUNE_ATTN_TARGET_WG, _CHUNK_MAX, _PIPE, ...
 AttnPlan plan_attention(int b, int B, int Hq, int Hkv, int d, int max_prefix, int data_rule) {
   return plan_attention_rows(b, data_rule == 2 ? B : 2 * B, Hq, Hkv, d, max_prefix);
 }
@@ -1140,11 +1140,11 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
     p.nwc = 4, p.qb = 2;
   }
   p.rows_per_wg = p.nwc * p.qb * 16;
-  p.xcd_remap = env_int("SIMSD_ATTN_XCD_REMAP", 1) != 0;  // tuning: keep a unit's splits on one XCD
-  p.rotate = env_int("SIMSD_ATTN_ROTATE", 1) != 0;        // tuning: per-unit starting prefix tile
+  p.xcd_remap = tuned(SIMSD_TUNE_ATTN_XCD_REMAP, 1) != 0;  // tuning: keep a unit's splits on one XCD
+  p.rotate = tuned(SIMSD_TUNE_ATTN_ROTATE, 1) != 0; // tuning: per-unit starting prefix tile
   p.row_slices = (M + p.rows_per_wg - 1) / p.rows_per_wg;
-  const int target = std::max(1, env_int("SIMSD_ATTN_TARGET_WG", 256));
-  const int chunk_max = std::max(TK, env_int("SIMSD_ATTN_CHUNK_MAX", 1 << 30) / TK * TK);
+  const int target = std::max(1, tuned(SIMSD_TUNE_ATTN_TARGET_WG, 256));
+  const int chunk_max = std::max(TK, tuned(SIMSD_TUNE_ATTN_CHUNK_MAX, 1 << 30) / TK * TK);
   const long units = static_cast<long>(b) * Hkv * p.row_slices;
   // A split shorter than a few tiles costs more in hand-off and merge than it
   // saves (b = 1, prefix 1024: 16 one-tile splits 19 us, 4 four-tile splits
@@ -1183,14 +1183,14 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
   const bool lpt_ok = nsplit == 1 && p.row_slices == 1 && b <= 64;
   const bool lpt_ring = p.qb == 1 && wgs > 256 && lpt_ok && d == 128;
   const int pipe_default = p.qb == 1 ? (wgs > 256 ? (lpt_ring ? 6 : 1) : 0) : (wgs <= 256 ? 9 : 0);
-  p.pipe = env_int("SIMSD_ATTN_PIPE", pipe_default);
+  p.pipe = tuned(SIMSD_TUNE_ATTN_PIPE, pipe_default);
   p.chunk = chunk;
   p.nsplit = nsplit;
-  // tuning: SIMSD_ATTN_LPT = 0 / 1 forces the longest-first order off / on
-  p.lpt = (env_int("SIMSD_ATTN_LPT", lpt_ring ? 1 : 0) != 0 && lpt_ok) ? 1 : 0;
+  // tuning: SIMSD_TUNE_ATTN_LPT = 0 / 1 forces the longest-first order off / on
+  p.lpt = (tuned(SIMSD_TUNE_ATTN_LPT, lpt_ring ? 1 : 0) != 0 && lpt_ok) ? 1 : 0;
   // tuning: prefix keys moved off split 0, which also takes the block tiles
-  // (SIMSD_ATTN_SHIFT; measured neutral on MI355X, so 0 by default)
-  p.shift = std::max(0, std::min(chunk / 2, env_int("SIMSD_ATTN_SHIFT", 0)));
+  // (SIMSD_TUNE_ATTN_SHIFT; measured neutral on MI355X, so 0 by default)
+  p.shift = std::max(0, std::min(chunk / 2, tuned(SIMSD_TUNE_ATTN_SHIFT, 0)));
   const size_t us = static_cast<size_t>(units);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   // The counter words sit in a region of fixed size at the start of every

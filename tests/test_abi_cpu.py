@@ -123,6 +123,26 @@ def test_workspace_sizes(lib):
     assert lib.simsd_accept_workspace(1, 8, 0) == 0
 
 
+def test_tuning_is_explicit_and_changes_only_what_it_names(lib):
+    # unknown keys and values below -1 are refused
+    assert lib.simsd_set_tuning(-1, 0) == 2
+    assert lib.simsd_set_tuning(9, 0) == 2
+    assert lib.simsd_set_tuning(0, -2) == 2
+    cfg = (16, 8, 32, 8, 128, 4096)
+    base = lib.simsd_verify_attention_workspace(*cfg)
+    # the environment is never read: setting a variable of the old tuning
+    # scheme changes nothing
+    os.environ["SIMSD_ATTN_TARGET_WG"] = "4096"
+    try:
+        assert lib.simsd_verify_attention_workspace(*cfg) == base
+    finally:
+        os.environ.pop("SIMSD_ATTN_TARGET_WG", None)
+    # an explicit override does (more splits, more partials), and -1 restores it
+    with binding.tuning(attn_target_wg=4096):
+        assert lib.simsd_verify_attention_workspace(*cfg) > base
+    assert lib.simsd_verify_attention_workspace(*cfg) == base
+
+
 def test_rope_host_errors(lib):
     f = lambda **kw: lib.simsd_rope_copy(kw.get("q", FAKE), kw.get("k", FAKE), kw.get("sp", FAKE),
                                          kw.get("b", 1), kw.get("B", 4), kw.get("Hq", 8),

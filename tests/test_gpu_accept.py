@@ -62,7 +62,7 @@ def test_many_forced_rejections(V):
 
 
 @pytest.mark.parametrize("V,b", [(5001, 64), (32768, 64), (151936, 24)])
-def test_segment_widths_agree_and_leave_workspace_zero(V, b, monkeypatch):
+def test_segment_widths_agree_and_leave_workspace_zero(V, b):
     # Every segment width (entries per thread 4 / 8 / 16) gives the oracle's
     # lengths and, outside counted CDF-boundary cases, its tokens; each call
     # leaves the whole workspace zero for the next one.
@@ -72,11 +72,11 @@ def test_segment_widths_agree_and_leave_workspace_zero(V, b, monkeypatch):
     dev = lambda a: torch.as_tensor(np.ascontiguousarray(a)).cuda()
     args = [dev(a) for a in (p, q, draft, tau, u)]
     ws = torch.zeros(binding.simsd_accept_workspace(b, 8, V), dtype=torch.uint8, device="cuda")
-    for per in ("4", "8", "16", "4"):
+    for per in (4, 8, 16, 4):
         say(f"  V={V} b={b} entries per thread {per}")
-        monkeypatch.setenv("SIMSD_ACCEPT_PER", per)
         status = torch.zeros(b, dtype=torch.int32, device="cuda")
-        L, corr = binding.simsd_accept(*args, status=status, workspace=ws)
+        with binding.tuning(accept_per=per):
+            L, corr = binding.simsd_accept(*args, status=status, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(L.cpu().numpy(), ref["accept_len"]), per
         assert np.array_equal(status.cpu().numpy(), ref["status"]), per

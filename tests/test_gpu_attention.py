@@ -3,7 +3,6 @@
 Tolerance: max-abs 2e-2 for bf16 output (bf16 inputs, fp32 accumulation);
 the fp32-output path is held to 4e-3 to separate kernel arithmetic from the
 final bf16 rounding."""
-import os
 
 import numpy as np
 import pytest
@@ -95,16 +94,16 @@ def test_shapes_match_oracle(shape, rule):
 
 
 @pytest.mark.parametrize("B", [8, 16], ids=["64_rows", "128_rows"])
-def test_every_kernel_variant_matches_oracle(B, monkeypatch):
-    # Each key-tile ring / wave layout the launcher can select (SIMSD_ATTN_PIPE)
-    # on a batch with several tiles per split, ragged tails and an empty prefix.
+def test_every_kernel_variant_matches_oracle(B):
+    # Each key-tile ring / wave layout the launcher can select (tuning key
+    # attn_pipe) on a batch with several tiles per split, ragged tails and an
+    # empty prefix.
     w = synth.custom(b=3, Hq=32, Hkv=8, d=128, B=B, prefix=(0, 2100))
     x = synth.make_inputs(w, with_accept=False, seed=31 + B)
     ref, ref_lse = run_oracle(x)
     for pipe in range(10):
-        monkeypatch.setenv("SIMSD_ATTN_PIPE", str(pipe))
-        monkeypatch.setenv("SIMSD_ATTN_CHUNK_MAX", "512")
-        out, lse = run_gpu(x, flags=binding.SIMSD_OUT_F32 | binding.SIMSD_KV_HEAD_MAJOR)
+        with binding.tuning(attn_pipe=pipe, attn_chunk_max=512):
+            out, lse = run_gpu(x, flags=binding.SIMSD_OUT_F32 | binding.SIMSD_KV_HEAD_MAJOR)
         compare(out, lse, ref, ref_lse, 0, TOL_F32, f"pipe {pipe}")
 
 
@@ -160,19 +159,12 @@ def test_deterministic_and_split_independent():
     a, _ = run_gpu(x, flags=binding.SIMSD_OUT_F32)
     b, _ = run_gpu(x, flags=binding.SIMSD_OUT_F32)
     assert torch.equal(a, b), "two identical calls differ"
-    old = os.environ.get("SIMSD_ATTN_TARGET_WG")
-    try:
-        for target in ("1", "4096"):
-            os.environ["SIMSD_ATTN_TARGET_WG"] = target
+    for target in (1, 4096):
+        with binding.tuning(attn_target_wg=target):
             c, _ = run_gpu(x, flags=binding.SIMSD_OUT_F32)
-            err = float((c - a).abs().max())
-            say(f"  target {target}: max diff vs default {err:.2e}")
-            assert err < 2e-3
-    finally:
-        if old is None:
-            os.environ.pop("SIMSD_ATTN_TARGET_WG", None)
-        else:
-            os.environ["SIMSD_ATTN_TARGET_WG"] = old
+        err = float((c - a).abs().max())
+        say(f"  target {target}: max diff vs default {err:.2e}")
+        assert err < 2e-3
 
 
 def test_status_bits():

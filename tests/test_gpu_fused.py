@@ -69,7 +69,7 @@ def table_falls_back(Hq, Hkv, d, B, rflags, flags):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-def test_fused_equals_two_calls_bit_exact(case, monkeypatch):
+def test_fused_equals_two_calls_bit_exact(case):
     b, Hq, Hkv, d, B, pre, rflags, flags = case
     say(f"fused rope+attention {case}")
     w = synth.custom(b=b, Hq=Hq, Hkv=Hkv, d=d, B=B, prefix=pre)
@@ -79,11 +79,10 @@ def test_fused_equals_two_calls_bit_exact(case, monkeypatch):
     g = prep(x, flags & binding.SIMSD_KV_HEAD_MAJOR)
     q0, k0 = g["q_blk"].clone(), g["k_blk"].clone()
     mp = int(pre[1])
-    if table_falls_back(Hq, Hkv, d, B, rflags, flags):
-        # the reference takes the variant the fused launch falls back to
-        monkeypatch.setenv("SIMSD_ATTN_PIPE", "7")
-    ref_out, ref_lse, ref_k = two_call(g, 10000.0, rflags, flags, mp)
-    monkeypatch.delenv("SIMSD_ATTN_PIPE", raising=False)
+    # the reference takes the variant the fused launch falls back to when its
+    # table does not fit beside the default ring
+    with binding.tuning(attn_pipe=7 if table_falls_back(Hq, Hkv, d, B, rflags, flags) else -1):
+        ref_out, ref_lse, ref_k = two_call(g, 10000.0, rflags, flags, mp)
     out, lse, k_rot = fused(g, 10000.0, rflags, flags, mp)
     torch.cuda.synchronize()
     assert torch.equal(g["q_blk"], q0) and torch.equal(g["k_blk"], k0), "inputs modified"
