@@ -59,7 +59,9 @@ typedef enum {
   SIMSD_ERR_ALIGN = 7,     /* a tensor pointer is not 16-byte aligned */
   SIMSD_ERR_LAUNCH = 8,    /* the HIP runtime refused a launch (see simsd_last_hip_error) */
   SIMSD_ERR_SCALE = 9,     /* rope_base <= 0 or a non-finite scale */
-  SIMSD_ERR_ALIAS = 10     /* an output overlaps an input it must not overlap */
+  SIMSD_ERR_ALIAS = 10,    /* an output overlaps an input it must not overlap */
+  SIMSD_ERR_SCRATCH = 11   /* simsd_verify_attention_noalloc: the sizes need more than the fixed
+                              scratch buffer holds */
 } simsd_status_t;
 
 /* Device status bits (int32 per sequence, OR-ed in). */
@@ -182,6 +184,35 @@ int simsd_verify_attention(const void* q_blk, const void* k_blk, const void* v_b
 /* Workspace bytes simsd_verify_attention (and simsd_verify_attention_rope)
  * needs for these sizes (0 on bad sizes). */
 size_t simsd_verify_attention_workspace(int b, int B, int Hq, int Hkv, int d, int max_prefix);
+
+/*
+ * simsd_verify_attention_noalloc -- simsd_verify_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and bit-identical results. The workspace is a
+ * fixed device array inside the library, SIMSD_NOALLOC_SCRATCH_BYTES per GPU,
+ * held by each GPU the library runs on until the process ends. Nothing is
+ * allocated or freed by the call.
+ *   - Sizes whose simsd_verify_attention_workspace exceeds
+ *     SIMSD_NOALLOC_SCRATCH_BYTES are refused with SIMSD_ERR_SCRATCH (the
+ *     headline shapes need at most 16.5 MiB: 8 sequences of 16384 cached
+ *     tokens with B = 16 and 32/8 heads of 128).
+ *   - The stream must belong to the current device. The first call on a
+ *     device looks up that device's copy of the array and enqueues, ahead of
+ *     its own kernels, a fill kernel that clears the counter region at its
+ *     start; every call leaves that region zero again.
+ *   - Every call on a GPU shares that GPU's array: calls that may overlap in
+ *     time on one GPU (other streams, other threads, concurrent replays of
+ *     captured graphs) race and must be serialised by the caller.
+ * Errors: those of simsd_verify_attention except _WORKSPACE, and
+ * SIMSD_ERR_SCRATCH.
+ */
+#define SIMSD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int simsd_verify_attention_noalloc(const void* q_blk, const void* k_blk, const void* v_blk,
+                                   const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                                   const int32_t* tau, void* out, float* lse, int b, int B, int Hq, int Hkv,
+                                   int d, int max_prefix, float scale, uint32_t flags, int32_t* status,
+                                   void* stream);
 
 /*
  * simsd_verify_attention_mask -- the same attention pass with the block mask

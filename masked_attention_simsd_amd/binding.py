@@ -35,7 +35,10 @@ EXPORTS = (
     "simsd_verify_attention_mask_workspace",
     "simsd_accept", "simsd_accept_workspace", "simsd_accept_logits", "simsd_accept_logits_workspace",
     "simsd_commit_kv", "simsd_status_string", "simsd_last_hip_error", "simsd_set_tuning",
+    "simsd_verify_attention_noalloc",
 )
+SIMSD_ERR_SCRATCH = 11
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class SimsdError(RuntimeError):
@@ -65,6 +68,8 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_verify_attention_rope.argtypes = [P, P, P, P, P, P, P, P, F, U, P, P, P, I, I, I, I, I, I,
                                                     F, U, P, P, Z, P]
         lib.simsd_verify_attention_rope.restype = I
+        lib.simsd_verify_attention_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, U, P, P]
+        lib.simsd_verify_attention_noalloc.restype = I
         lib.simsd_verify_attention_workspace.argtypes = [I, I, I, I, I, I]
         lib.simsd_verify_attention_workspace.restype = Z
         lib.simsd_verify_attention_mask.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, U, P, P, Z, P]
@@ -255,6 +260,16 @@ def simsd_verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, ta
                       tau, out, lse, max_prefix, scale, flags, status, workspace, stream, None)
 
 
+def simsd_verify_attention_noalloc(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse=None,
+                                   max_prefix: int | None = None, scale: float = 0.0, flags: int = 0,
+                                   status=None, stream=None):
+    """simsd_verify_attention without a workspace argument: the library uses
+    its fixed per-GPU scratch buffer and allocates nothing (so `out` must be
+    given). Calls on one GPU must not overlap."""
+    return _attention("simsd_verify_attention_noalloc", q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets,
+                      tau, out, lse, max_prefix, scale, flags, status, None, stream, "noalloc")
+
+
 def simsd_verify_attention_rope(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, start_pos,
                                 rope_base: float = 10000.0, rope_flags: int = 0, k_rot=None, out=None,
                                 lse=None, max_prefix: int | None = None, scale: float = 0.0,
@@ -293,8 +308,10 @@ def _attention(fn, q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, 
     if max_prefix is None:
         max_prefix = _max_prefix(prefix_offsets, b)
     out_f32 = bool(flags & SIMSD_OUT_F32)
-    if out is None:
+    if out is None and rope != "noalloc":
         out = torch.empty_like(q_blk, dtype=torch.float32 if out_f32 else torch.bfloat16)
+    if out is None:
+        raise ValueError("simsd_verify_attention_noalloc needs an output tensor (it allocates nothing)")
     _need(out, "out", torch.float32 if out_f32 else torch.bfloat16, 4)
     if tuple(out.shape) != tuple(q_blk.shape):
         raise ValueError("out shape must equal q_blk shape")
@@ -302,14 +319,23 @@ def _attention(fn, q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, 
         _need(lse, "lse", torch.float32, 3)
     if status is not None:
         _need(status, "status", torch.int32, 1)
-    need = simsd_verify_attention_workspace(b, B, Hq, Hkv, d, max_prefix)
-    if workspace is None:
-        workspace = attention_workspace(q_blk.device, need)
+    if rope == "noalloc":
+        if out is None:
+            raise ValueError("simsd_verify_attention_noalloc needs an output tensor (it allocates nothing)")
+    else:
+        need = simsd_verify_attention_workspace(b, B, Hq, Hkv, d, max_prefix)
+        if workspace is None:
+            workspace = attention_workspace(q_blk.device, need)
     head = (_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre) if k_pre.numel() else None,
             _ptr(v_pre) if v_pre.numel() else None, _ptr(prefix_offsets), _ptr(tau))
+    lib = load_library()
+    if rope == "noalloc":
+        rc = lib.simsd_verify_attention_noalloc(*head, _ptr(out), _ptr(lse), b, B, Hq, Hkv, d, int(max_prefix),
+                                                float(scale), flags, _ptr(status), _stream(stream))
+        _check(fn, rc)
+        return out
     tail = (_ptr(out), _ptr(lse), b, B, Hq, Hkv, d, int(max_prefix), float(scale), flags, _ptr(status),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    lib = load_library()
     if rope is None:
         rc = lib.simsd_verify_attention(*head, *tail)
     else:

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "simsd_internal.h"
 
@@ -59,7 +60,7 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
                           const void* v_pre, const int32_t* prefix_offsets, const int32_t* tau,
                           void* out, float* lse, int b, int B, int Hq, int Hkv, int d, int max_prefix,
                           float scale, uint32_t flags, int32_t* status, void* workspace,
-                          size_t ws_bytes, void* stream, const RopeIn* rope) {
+                          size_t ws_bytes, void* stream, const RopeIn* rope, bool check_only = false) {
   if (!q_blk || !k_blk || !v_blk || !prefix_offsets || !tau || !out) return SIMSD_ERR_NULL;
   if (max_prefix > 0 && (!k_pre || !v_pre)) return SIMSD_ERR_NULL;
   int rc = check_common(b, B, Hq, Hkv, d);
@@ -88,7 +89,10 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
     }
   }
   const simsd::AttnPlan plan = simsd::plan_attention(b, B, Hq, Hkv, d, max_prefix, static_cast<int>(rule));
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || ws_bytes < plan.total_bytes)
+  if (static_cast<long>(b) * Hkv * plan.row_slices > simsd::kAttnMaxUnits ||
+      static_cast<long>(b) * Hkv * plan.row_slices * plan.nsplit > (1L << 30))
+    return SIMSD_ERR_SIZE;
+  if (check_only || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || ws_bytes < plan.total_bytes)
     return SIMSD_ERR_WORKSPACE;
 
   simsd::AttnArgs a{};
@@ -142,6 +146,49 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
     a.k_rot = static_cast<uint16_t*>(rope->k_rot);
   }
   return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
+}
+
+// ---- the allocation-free attention entry point ----
+// One fixed device buffer, of this size, stands in for the caller's workspace
+// (every GPU the library runs on holds its own copy until the process ends).
+constexpr size_t kScratchBytes = static_cast<size_t>(SIMSD_NOALLOC_SCRATCH_BYTES);
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes >= static_cast<size_t>(simsd::kAttnMaxUnits) * 4,
+              "the scratch holds at least the counter region");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};  // the device address of `scratch` on each device, once known
+
+__global__ void zero_words_kernel(uint4* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The address of the current device's scratch array. On the first call on a
+// device it is looked up (hipGetSymbolAddress, with that device current) and
+// the counter region at its start is cleared by a fill kernel on `stream`,
+// ahead of the kernels the call then enqueues there; every attention call
+// leaves that region zero again.
+int scratch_of_current_device(void** out, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return SIMSD_ERR_SIZE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return launch_status(e);
+    if (!p) return launch_status(hipErrorInvalidSymbol);
+    const int n = simsd::kAttnMaxUnits * 4 / 16;  // counter words, 16 bytes per thread
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<uint4*>(p), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_status(e);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SIMSD_OK;
 }
 
 }  // namespace
@@ -208,6 +255,26 @@ int simsd_verify_attention_rope(const void* q_blk, const void* k_blk, const void
   return verify_attention_impl(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, b, B, Hq,
                                Hkv, d, max_prefix, scale, flags, status, workspace, ws_bytes, stream,
                                &rope);
+}
+
+int simsd_verify_attention_noalloc(const void* q_blk, const void* k_blk, const void* v_blk,
+                                   const void* k_pre, const void* v_pre, const int32_t* prefix_offsets,
+                                   const int32_t* tau, void* out, float* lse, int b, int B, int Hq, int Hkv,
+                                   int d, int max_prefix, float scale, uint32_t flags, int32_t* status,
+                                   void* stream) {
+  // sizes and arguments first (nothing touched on a bad call), then the
+  // scratch size the plan needs against the fixed buffer
+  const size_t need = simsd_verify_attention_workspace(b, B, Hq, Hkv, d, max_prefix);
+  int rc = verify_attention_impl(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, b, B, Hq,
+                                 Hkv, d, max_prefix, scale, flags, status, nullptr, 0, stream, nullptr,
+                                 /*check_only=*/true);
+  if (rc != SIMSD_ERR_WORKSPACE) return rc;  // an argument error, reported as for simsd_verify_attention
+  if (need == 0 || need > kScratchBytes) return SIMSD_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  return verify_attention_impl(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau, out, lse, b, B, Hq, Hkv,
+                               d, max_prefix, scale, flags, status, ws, kScratchBytes, stream, nullptr);
 }
 
 size_t simsd_verify_attention_mask_workspace(int b, int R, int Hq, int Hkv, int d, int max_prefix) {
@@ -418,6 +485,7 @@ const char* simsd_status_string(int code) {
     case SIMSD_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case SIMSD_ERR_SCALE: return "rope_base or scale out of range";
     case SIMSD_ERR_ALIAS: return "an output overlaps an input it must not overlap";
+    case SIMSD_ERR_SCRATCH: return "the sizes need more scratch than the fixed device buffer holds";
     default: return "unknown status";
   }
 }

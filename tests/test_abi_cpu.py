@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(11):
+    for code in range(12):
         assert lib.simsd_status_string(code)
     assert lib.simsd_status_string(0) == b"ok"
 
@@ -103,6 +103,31 @@ def test_fused_rope_attention_host_errors(lib):
     assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 4096)) == 10
     assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 8192)) != 10
     assert lib.simsd_status_string(10)
+
+
+def test_noalloc_attention_host_errors(lib):
+    # the same argument checks as simsd_verify_attention, before any HIP call;
+    # sizes whose workspace exceeds the fixed scratch buffer are refused
+    f = lambda **kw: lib.simsd_verify_attention_noalloc(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("kp", FAKE), FAKE, FAKE, FAKE, kw.get("out", FAKE), None,
+        kw.get("b", 2), kw.get("B", 4), kw.get("Hq", 8), kw.get("Hkv", 2), kw.get("d", 128),
+        kw.get("maxp", 100), 0.0, kw.get("flags", 0), None, None)
+    assert f(q=None) == 1
+    assert f(out=None) == 1
+    assert f(b=0) == 2
+    assert f(Hq=9) == 3
+    assert f(d=96) == 4
+    assert f(flags=3) == 5
+    assert f(q=MISALIGNED) == 7
+    # the split plan keeps partials near one workgroup per CU (16.5 MiB at
+    # most for 8 sequences, B = 16, 32/8 heads); forcing 4096 workgroups asks
+    # for far more than the fixed buffer
+    big = dict(b=8, B=16, Hq=32, Hkv=8, maxp=16384)
+    assert lib.simsd_verify_attention_workspace(8, 16, 32, 8, 128, 16384) <= binding.NOALLOC_SCRATCH_BYTES
+    with binding.tuning(attn_target_wg=4096):
+        assert lib.simsd_verify_attention_workspace(8, 16, 32, 8, 128, 16384) > binding.NOALLOC_SCRATCH_BYTES
+        assert f(**big) == binding.SIMSD_ERR_SCRATCH
+    assert lib.simsd_status_string(binding.SIMSD_ERR_SCRATCH) != b"unknown status"
 
 
 def test_workspace_sizes(lib):
