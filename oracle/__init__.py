@@ -29,6 +29,13 @@ Parity status of each function (what pins it, all in ``tests/test_oracle_*``):
   accept_logits           softmax_rows then accept (both pinned), plus the
                           decision margins a differently rounded softmax may
                           cross (ratio_boundary).
+  next_positions / committed_positions
+                          integer bookkeeping of the round loop: pinned by
+                          closed forms (L = 0, L = B, identity order), the
+                          B smallest uncached positions found by brute force,
+                          and over several rounds with partial acceptance the
+                          committed and next-round positions covering a
+                          contiguous range exactly once.
   commit_kv / pack_regions
                           pure row movement (numpy indexing, no arithmetic):
                           pinned by closed forms (identity and reversed tau,
@@ -95,7 +102,7 @@ def _load():
         lib.simsd_oracle_attention_row.restype = None
         lib.simsd_oracle_verify_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, D, I, P, P]
         lib.simsd_oracle_verify_attention.restype = I
-        lib.simsd_oracle_rope_copy.argtypes = [P, P, I, I, I, I, D, I, I]
+        lib.simsd_oracle_rope_copy.argtypes = [P, P, P, I, I, I, I, D, I, I]
         lib.simsd_oracle_rope_copy.restype = None
         lib.simsd_oracle_accept.argtypes = [P, P, P, P, P, I, I, I, P, P, P, P]
         lib.simsd_oracle_accept.restype = None
@@ -218,12 +225,22 @@ def verify_attention(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offsets, tau,
 
 def rope_copy(x, start_pos, base: float = 10000.0, interleaved: bool = False,
               no_copy: bool = False) -> np.ndarray:
-    """Rotated copy of x [b][2B][H][d] (fp64)."""
+    """Rotated copy of x [b][2B][H][d] (fp64). start_pos is [b] (D_k and D~_k
+    at start_pos[s] + k - 1) or [b][B] (explicit positions: D_k and D~_k at
+    start_pos[s][k-1])."""
     y = _f64(x).copy()
     sp = _i32(start_pos)
     b, twoB, H, d = y.shape
-    _load().simsd_oracle_rope_copy(_p(y), _p(sp), b, twoB // 2, H, d, float(base),
-                                   int(bool(interleaved)), int(bool(no_copy)))
+    if sp.ndim == 2:
+        if no_copy:
+            raise ValueError("the no-copy ablation takes consecutive positions only")
+        if sp.shape != (b, twoB // 2):
+            raise ValueError("positions must be [b][B]")
+        _load().simsd_oracle_rope_copy(_p(y), None, _p(sp), b, twoB // 2, H, d, float(base),
+                                       int(bool(interleaved)), 0)
+    else:
+        _load().simsd_oracle_rope_copy(_p(y), _p(sp), None, b, twoB // 2, H, d, float(base),
+                                       int(bool(interleaved)), int(bool(no_copy)))
     return y
 
 
@@ -318,6 +335,54 @@ def pack_regions(cache, offsets, lens, head_major: bool = False):
     po = np.zeros(b + 1, dtype=np.int32)
     po[1:] = np.cumsum(ln)
     return packed, po
+
+
+def next_positions(pos, tau, accept_len):
+    """Response positions of the next round of each sequence ([nl]/[fr]
+    Methodologie 1 and 4: each pair (D_k, D~_k) is one response position;
+    the longest prefix accepted along the temporal order is committed and the
+    round repeats over what is still open).
+
+    pos [b][B] holds the positions this round verified, tau [b][B] its step
+    labels, accept_len [b] the accepted lengths L. The drafts at tau^-1(1..L)
+    enter the cache; the next round verifies the B smallest positions not in
+    the cache: when L < B, first the position tau^-1(L+1), whose correction
+    token is committed but has no key/value row yet (the next round computes
+    it, as that round's data token at temporal step 1), then the other open
+    positions tau^-1(L+2..B) in increasing order, then L positions following
+    the largest one of this block. A sequence whose tau is not a permutation or
+    whose L is outside 0..B commits nothing and keeps its block.
+
+    Returns next [b][B] int32."""
+    ps, t, L_all = _i32(pos), _i32(tau), _i32(accept_len)
+    b, B = t.shape
+    nxt = ps.copy()
+    for s in range(b):
+        inv, ok = tau_inverse(t[s])
+        L = int(L_all[s])
+        if not ok or L < 0 or L > B:
+            continue
+        frontier = int(ps[s].max()) + 1
+        row = []
+        if L < B:
+            row.append(int(ps[s, inv[L]]))  # the correction's position
+            row += sorted(int(ps[s, inv[j]]) for j in range(L + 1, B))
+        row += [frontier + i for i in range(L)]
+        nxt[s] = row
+    return nxt
+
+
+def committed_positions(pos, tau, accept_len):
+    """The positions whose key/value rows a commit appends, per sequence, in
+    temporal order: pos[s][tau^-1(t)] for t = 1..L (empty for a sequence that
+    commits nothing)."""
+    ps, t, L_all = _i32(pos), _i32(tau), _i32(accept_len)
+    out = []
+    for s in range(t.shape[0]):
+        inv, ok = tau_inverse(t[s])
+        L = int(L_all[s])
+        out.append([int(ps[s, inv[j]]) for j in range(L)] if ok and 0 <= L <= t.shape[1] else [])
+    return out
 
 
 def commit_kv(k_blk, v_blk, tau, accept_len, k_cache, v_cache, cache_offsets, cache_lens,

@@ -174,23 +174,26 @@ int simsd_oracle_verify_attention(const double* q_blk, const double* k_blk, cons
 /* RoPE with the copy rule ([nl]/[fr] Methodologie 3, position-encoding
  * alignment: each mask slot D~_k takes the RoPE index of its paired data
  * token D_k).
- * Positions: D_k and D~_k (k = 1..B) both sit at start_pos[s] + k - 1. With
- * no_copy set (an ablation the pages report but do not define), D~_k instead
- * sits at start_pos[s] + B + k - 1, i.e. the mask section is numbered after
- * the data section as a plain concatenation would.
+ * Positions: D_k and D~_k (k = 1..B) both sit at start_pos[s] + k - 1, or,
+ * when `positions` is given ([b][B]), both at positions[s][k-1] (each pair is
+ * one response position, Methodologie 1; a later round of the same block
+ * re-verifies the positions still open, wherever they lie). With no_copy set
+ * (an ablation the pages report but do not define; only with consecutive
+ * positions), D~_k instead sits at start_pos[s] + B + k - 1, i.e. the mask
+ * section is numbered after the data section as a plain concatenation would.
  * Rotation (standard rotary embedding, fp64): frequency i = 0..d/2-1 has
  * inv_freq_i = base^(-2i/d) and angle = pos * inv_freq_i. Rotate-half pairs
  * element i with element i + d/2; interleaved pairs 2i with 2i+1. Each pair
  * (x, y) becomes (x cos - y sin, y cos + x sin).
  *   x [b][2B][H][d] rotated in place (used for Q with H = Hq and for K with
  *   H = Hkv). */
-void simsd_oracle_rope_copy(double* x, const int32_t* start_pos, int b, int B, int H, int d,
-                            double base, int interleaved, int no_copy) {
+void simsd_oracle_rope_copy(double* x, const int32_t* start_pos, const int32_t* positions, int b, int B,
+                            int H, int d, double base, int interleaved, int no_copy) {
   int half = d / 2;
   for (int s = 0; s < b; ++s) {
     for (int r = 0; r < 2 * B; ++r) {
       int k = r < B ? r : r - B; /* 0-based response position of this row */
-      long pos = (long)start_pos[s] + k;
+      long pos = positions ? (long)positions[(size_t)s * B + k] : (long)start_pos[s] + k;
       if (no_copy && r >= B) pos += B;
       for (int h = 0; h < H; ++h) {
         double* v = x + (((size_t)s * 2 * B + r) * H + h) * d;

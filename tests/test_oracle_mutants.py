@@ -48,7 +48,8 @@ MUTANTS = {
     "rope_no_copy_rule": [("int k = r < B ? r : r - B;", "int k = r;")],
     "rope_pairs_mirrored": [("int bb = interleaved ? 2 * i + 1 : i + half;",
                              "int bb = interleaved ? 2 * i + 1 : d - 1 - i;")],
-    "rope_position_off_by_one": [("long pos = (long)start_pos[s] + k;", "long pos = (long)start_pos[s] + k + 1;")],
+    "rope_position_off_by_one": [("(long)start_pos[s] + k;", "(long)start_pos[s] + k + 1;")],
+    "rope_positions_of_the_first_pair": [("(long)positions[(size_t)s * B + k]", "(long)positions[(size_t)s * B]")],
     # acceptance ([nl]/[fr] Methodologie 4)
     "accept_non_strict": [("if (!(us[t - 1] < r)) {", "if (!(us[t - 1] <= r)) {")],
     "accept_in_position_order": [("      int k = inv[t - 1];\n", "      int k = t - 1;\n")],
@@ -86,6 +87,14 @@ PY_MUTANTS = {
     "commit_overflow_off_by_one": [("int(ln[s]) + L > cap", "int(ln[s]) + L > cap + 1")],
     "commit_values_from_keys": [("vc[:, row] = vb[s, k]", "vc[:, row] = kb[s, k]"),
                                 ("vc[row] = vb[s, k]", "vc[row] = kb[s, k]")],
+    "next_correction_not_first": [("row.append(int(ps[s, inv[L]]))  # the correction's position\n", ""),
+                                  ("for j in range(L + 1, B))", "for j in range(L, B))")],
+    "next_frontier_off_by_one": [("frontier = int(ps[s].max()) + 1", "frontier = int(ps[s].max())")],
+    "next_reopens_an_accepted_position": [("for j in range(L + 1, B))", "for j in range(L - 1 if L else 1, B))"),
+                                          ("row += [frontier + i for i in range(L)]",
+                                           "row += [frontier + i for i in range(L)]\n        row = row[:B]")],
+    "committed_in_position_order": [("out.append([int(ps[s, inv[j]]) for j in range(L)]",
+                                     "out.append([int(ps[s, j]) for j in range(L)]")],
     "pack_whole_regions": [("np.arange(off[s], off[s] + ln[s])", "np.arange(off[s], off[s + 1])")],
     "pack_offsets_of_regions": [("po[1:] = np.cumsum(ln)", "po[1:] = np.cumsum(np.diff(off))")],
 }
