@@ -387,8 +387,10 @@ def main():
     kc, vc = binding.kv_pair_views(kvc)
     ext = torch.cat([torch.arange(b + 1, dtype=torch.int32, device=dev) * cap,
                      torch.zeros(b, dtype=torch.int32, device=dev)])
+    # the round's positions, advanced in place to the next round's by every call
+    cpos = (base["start_pos"][:, None] + torch.arange(B, device=dev, dtype=torch.int32)[None, :]).contiguous()
     commit_call = (P(base["k_blk"]), P(base["v_blk"]), P(base["tau"]), P(par_L), P(kc), P(vc), P(ext),
-                   P(ext[b + 1:]), b, B, Hkv, d, KV_LAYOUT, None, hs)
+                   P(ext[b + 1:]), P(cpos), P(cpos), b, B, Hkv, d, KV_LAYOUT, None, hs)
     rows = int(par_L.sum().item())
     calls_commit = [(commit_call,)]
     saved = calls

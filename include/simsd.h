@@ -80,6 +80,8 @@ typedef enum {
 #define SIMSD_ROPE_HALF 0u        /* rotate-half pairing (i, i + d/2) (default) */
 #define SIMSD_ROPE_INTERLEAVED 1u /* pairing (2i, 2i+1) */
 #define SIMSD_ROPE_NO_COPY 2u     /* ablation: D~_k at start + B + k - 1 instead of start + k - 1 */
+#define SIMSD_ROPE_POSITIONS 4u   /* start_pos holds one position per pair, int32 [b][B]: D_k and D~_k
+                                     at start_pos[s][k-1] (a later round of a block; not with NO_COPY) */
 
 /* simsd_verify_attention flags: data-row rule (2 bits) | output dtype | cache layout */
 #define SIMSD_DATA_CAUSAL 0u /* D_i sees the prefix and D_j with tau(j) <= tau(i) (default) */
@@ -106,6 +108,11 @@ typedef enum {
  *   start_pos  int32 [b]: position of D_1 of each sequence (normally its
  *              prefix length P_s). D_k and D~_k both sit at start_pos + k - 1;
  *              with SIMSD_ROPE_NO_COPY, D~_k sits at start_pos + B + k - 1.
+ *              With SIMSD_ROPE_POSITIONS it is int32 [b][B] instead, one
+ *              position per pair (each pair is one response position,
+ *              Methodologie 1): D_k and D~_k both sit at start_pos[s][k-1].
+ *              A later round of a block verifies the positions still open,
+ *              wherever they lie; simsd_commit_kv writes them.
  *   rope_base  base of the frequencies: frequency i = 0..d/2-1 turns by
  *              pos * rope_base^(-2i/d) radians. Angles, cos/sin and the
  *              rotation are evaluated in fp64; each result is rounded to bf16
@@ -113,7 +120,8 @@ typedef enum {
  *   flags      SIMSD_ROPE_* bits.
  * The cached prefix keys are not touched (they were rotated when cached).
  * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, heads<1), _HEAD_DIM,
- * _FLAGS, _SCALE (rope_base <= 0 or not finite), _ALIGN, _LAUNCH.
+ * _FLAGS (unknown bits, or NO_COPY with POSITIONS), _SCALE (rope_base <= 0 or
+ * not finite), _ALIGN, _LAUNCH.
  */
 int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, int B, int Hq,
                     int Hkv, int d, float rope_base, uint32_t flags, void* stream);
@@ -254,7 +262,8 @@ size_t simsd_verify_attention_mask_workspace(int b, int R, int Hq, int Hkv, int 
  * bit-identical to the two-call sequence.
  *
  *   q_blk, k_blk   bf16 [b][2B][Hq|Hkv][d] BEFORE RoPE (read only)
- *   start_pos, rope_base, rope_flags  as for simsd_rope_copy
+ *   start_pos, rope_base, rope_flags  as for simsd_rope_copy (with
+ *                  SIMSD_ROPE_POSITIONS, one position per pair, [b][B])
  *   k_rot          optional bf16 [b][2B][Hkv][d] output: the rotated block
  *                  keys (what simsd_rope_copy would leave in k_blk; the rows a
  *                  KV-cache commit appends). Must not overlap k_blk. NULL to
@@ -356,10 +365,11 @@ size_t simsd_accept_logits_workspace(int b, int B, int V);
 
 /*
  * simsd_commit_kv -- commit the accepted drafts of a verification round to the
- * KV cache, so that the next round verifies against them ([nl]/[fr]
+ * KV cache and name the positions the next round verifies ([nl]/[fr]
  * Methodologie 4, Acceptance / Acceptation: the longest prefix accepted along
- * the temporal order is committed and the round repeats; compatibility with a
- * KV cache, [nl] Belangrijkste Bijdragen 3 / [fr] Principales Contributions).
+ * the temporal order is committed and the round repeats; each pair (D_k, D~_k)
+ * is one response position, Methodologie 1; compatibility with a KV cache,
+ * [nl] Belangrijkste Bijdragen 3 / [fr] Principales Contributions).
  *
  * Sequence s accepted its first L = accept_len[s] drafts in temporal order,
  * the data tokens D_k with tau(k) <= L. Their key and value rows (block rows
@@ -368,6 +378,18 @@ size_t simsd_accept_logits_workspace(int b, int B, int V);
  * the sequence's cache region, and cache_lens[s] grows by L. Under the
  * default data-row rule (SIMSD_DATA_CAUSAL) each of these rows was computed
  * from exactly the context a token-by-token decode in temporal order gives it.
+ * The order of rows inside a region does not matter to attention (each row
+ * carries its position in its rotated key).
+ *
+ * The round loop (this library's reading of "the process repeats"): the next
+ * round verifies the B smallest positions not in the cache. When L < B, the
+ * first of them is the rejected step's position tau^-1(L+1): its correction
+ * token is committed but has no key/value row yet, so the caller places it as
+ * that round's data token at temporal step 1, with the draft probability of
+ * that position equal to the target's (standard rejection sampling then
+ * accepts it with probability one), and the next commit appends its row.
+ * Then come the other open positions (labels > L + 1) in increasing order,
+ * then L positions following this block's largest.
  *
  *   k_blk, v_blk     bf16 [b][2B][Hkv][d] (rows 0..B-1 are D_1..D_B)
  *   tau              int32 [b][B]
@@ -384,21 +406,32 @@ size_t simsd_accept_logits_workspace(int b, int B, int V);
  *                    rows). Laid out right after the region bounds
  *                    (cache_lens = cache_offsets + b + 1), the same array
  *                    serves as the prefix_offsets of simsd_verify_attention
- *                    with SIMSD_PREFIX_LENS and as the start_pos of the next
- *                    round.
- *   flags            SIMSD_KV_HEAD_MAJOR or 0
+ *                    with SIMSD_PREFIX_LENS.
+ *   pos              int32 [b][B]: the positions of this round's pairs (what
+ *                    simsd_rope_copy took); required with next_pos, else
+ *                    unused and may be NULL
+ *   next_pos         optional int32 [b][B] out: the next round's positions
+ *                    as above (pass it to simsd_rope_copy /
+ *                    simsd_verify_attention_rope with SIMSD_ROPE_POSITIONS).
+ *                    It may be pos itself (updated in place). A sequence with
+ *                    a status bit from this call keeps its block (next_pos =
+ *                    pos). Positions stay below 2^31 - B.
+ *   flags            SIMSD_KV_HEAD_MAJOR | SIMSD_KV_PAIRED or 0
  *   status           optional int32 [b]; SIMSD_DEV_BAD_TAU or
  *                    SIMSD_DEV_COMMIT_OVERFLOW (L outside 0..B, a negative
  *                    length, or L more rows do not fit the region): nothing of
  *                    that sequence is written and its length is kept.
- * The cache must not overlap k_blk / v_blk, and cache_lens must not overlap
- * tau, accept_len or cache_offsets (SIMSD_ERR_ALIAS).
- * Errors: SIMSD_ERR_NULL, _SIZE (b<1, B not in 1..64, Hkv<1), _HEAD_DIM,
- * _FLAGS, _ALIGN (bf16 tensors 16-byte aligned), _LAUNCH.
+ * The cache must not overlap k_blk / v_blk; cache_lens must not overlap tau,
+ * accept_len or cache_offsets, and next_pos no input other than pos itself
+ * (SIMSD_ERR_ALIAS).
+ * Errors: SIMSD_ERR_NULL (next_pos without pos, ...), _SIZE (b<1, B not in
+ * 1..64, Hkv<1), _HEAD_DIM, _FLAGS, _ALIGN (bf16 tensors 16-byte aligned),
+ * _ALIAS, _LAUNCH.
  */
 int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, const int32_t* accept_len,
-                    void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens, int b,
-                    int B, int Hkv, int d, uint32_t flags, int32_t* status, void* stream);
+                    void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens,
+                    const int32_t* pos, int32_t* next_pos, int b, int B, int Hkv, int d, uint32_t flags,
+                    int32_t* status, void* stream);
 
 /*
  * simsd_set_tuning -- override one choice of the kernel plans, process-wide,

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsimsd.so")
 
 # flag and status values, as in include/simsd.h
-SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY = 0, 1, 2
+SIMSD_ROPE_HALF, SIMSD_ROPE_INTERLEAVED, SIMSD_ROPE_NO_COPY, SIMSD_ROPE_POSITIONS = 0, 1, 2, 4
 SIMSD_DATA_CAUSAL, SIMSD_DATA_BIDIR, SIMSD_DATA_SKIP, SIMSD_OUT_F32 = 0, 1, 2, 4
 SIMSD_KV_HEAD_MAJOR, SIMSD_PREFIX_LENS, SIMSD_KV_PAIRED = 8, 16, 32
 SIMSD_DEV_BAD_TAU, SIMSD_DEV_ZERO_RESIDUAL, SIMSD_DEV_Q_ZERO = 1, 2, 4
@@ -82,7 +82,7 @@ def load_library(path: str = LIB_PATH):
         lib.simsd_accept_workspace.restype = Z
         lib.simsd_accept_logits.argtypes = [P, P, F, P, P, P, I, I, I, P, P, P, P, Z, P]
         lib.simsd_accept_logits.restype = I
-        lib.simsd_commit_kv.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, U, P, P]
+        lib.simsd_commit_kv.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, U, P, P]
         lib.simsd_commit_kv.restype = I
         lib.simsd_accept_logits_workspace.argtypes = [I, I, I]
         lib.simsd_accept_logits_workspace.restype = Z
@@ -193,18 +193,29 @@ def _max_prefix(prefix_offsets, b: int) -> int:
     return int((off[1:] - off[:-1]).max()) if b > 0 else 0
 
 
+def _need_positions(start_pos, b, B, flags):
+    """start_pos: int32 [b], or [b][B] (one position per pair) with SIMSD_ROPE_POSITIONS."""
+    if flags & SIMSD_ROPE_POSITIONS:
+        _need(start_pos, "start_pos", torch.int32, 2)
+        if tuple(start_pos.shape) != (b, B):
+            raise ValueError("with SIMSD_ROPE_POSITIONS start_pos must be [b][B]")
+    else:
+        _need(start_pos, "start_pos", torch.int32, 1)
+        if start_pos.shape[0] != b:
+            raise ValueError("start_pos must have b entries")
+
+
 def simsd_rope_copy(q_blk, k_blk, start_pos, rope_base: float = 10000.0, flags: int = 0,
                     stream=None):
     """In-place RoPE with the copy rule. q_blk [b][2B][Hq][d], k_blk [b][2B][Hkv][d] bf16,
-    start_pos int32 [b]."""
+    start_pos int32 [b] (pair k at start_pos[s] + k), or [b][B] positions with
+    SIMSD_ROPE_POSITIONS."""
     _need(q_blk, "q_blk", torch.bfloat16, 4)
     _need(k_blk, "k_blk", torch.bfloat16, 4)
-    _need(start_pos, "start_pos", torch.int32, 1)
     b, twoB, Hq, d = q_blk.shape
     if twoB % 2 or k_blk.shape[0] != b or k_blk.shape[1] != twoB or k_blk.shape[3] != d:
         raise ValueError("q_blk / k_blk shapes disagree")
-    if start_pos.shape[0] != b:
-        raise ValueError("start_pos must have b entries")
+    _need_positions(start_pos, b, twoB // 2, flags)
     rc = load_library().simsd_rope_copy(_ptr(q_blk), _ptr(k_blk), _ptr(start_pos), b, twoB // 2,
                                         Hq, k_blk.shape[2], d, float(rope_base), flags,
                                         _stream(stream))
@@ -277,9 +288,7 @@ def simsd_verify_attention_rope(q_blk, k_blk, v_blk, k_pre, v_pre, prefix_offset
     """RoPE-copy fused into verify attention: q_blk / k_blk are the block rows
     BEFORE RoPE and are not modified; k_rot (optional, [b][2B][Hkv][d] bf16,
     not overlapping k_blk) receives the rotated block keys. Returns out."""
-    _need(start_pos, "start_pos", torch.int32, 1)
-    if start_pos.shape[0] != q_blk.shape[0]:
-        raise ValueError("start_pos must have b entries")
+    _need_positions(start_pos, q_blk.shape[0], q_blk.shape[1] // 2, rope_flags)
     if k_rot is not None:
         _need(k_rot, "k_rot", torch.bfloat16, 4)
         if tuple(k_rot.shape) != tuple(k_blk.shape):
@@ -460,19 +469,22 @@ def simsd_accept_logits(target_logits, draft_logits, draft_tokens, tau, uniforms
 def cache_offsets_with_lens(offsets, lens):
     """One int32 device array [2b+1]: region bounds then used lengths. Pass it
     as prefix_offsets with SIMSD_PREFIX_LENS; its tail view ([b+1:]) is the
-    cache_lens of simsd_commit_kv and the start_pos of the next round."""
+    cache_lens of simsd_commit_kv (and, before the first round, the start
+    position of each sequence's first block)."""
     return torch.cat([offsets.to(torch.int32), lens.to(torch.int32)]).contiguous()
 
 
 def simsd_commit_kv(k_blk, v_blk, tau, accept_len, k_cache, v_cache, cache_offsets, cache_lens,
-                    flags: int = 0, status=None, stream=None):
+                    pos=None, next_pos=None, flags: int = 0, status=None, stream=None):
     """Append each sequence's accepted drafts (tau(k) <= accept_len[s]) to its
-    cache region, in temporal order, and advance cache_lens in place.
+    cache region, in temporal order, and advance cache_lens in place; with
+    next_pos, also write the positions the next round verifies.
 
     k_blk / v_blk [b][2B][Hkv][d] bf16; k_cache / v_cache [C][Hkv][d] (or
     [Hkv][C][d] with SIMSD_KV_HEAD_MAJOR) bf16; cache_offsets int32 [b+1];
     cache_lens int32 [b] (may be a view into the array built by
-    cache_offsets_with_lens)."""
+    cache_offsets_with_lens); pos / next_pos int32 [b][B] (this round's
+    positions and the next round's; next_pos may be pos)."""
     for t, n in ((k_blk, "k_blk"), (v_blk, "v_blk")):
         _need(t, n, torch.bfloat16, 4)
     _need_kv(k_cache, v_cache, ("k_cache", "v_cache"), flags)
@@ -490,7 +502,12 @@ def simsd_commit_kv(k_blk, v_blk, tau, accept_len, k_cache, v_cache, cache_offse
         raise ValueError("inconsistent shapes")
     if status is not None:
         _need(status, "status", torch.int32, 1)
+    for t, n in ((pos, "pos"), (next_pos, "next_pos")):
+        if t is not None:
+            _need(t, n, torch.int32, 2)
+            if tuple(t.shape) != (b, B):
+                raise ValueError(f"{n} must be [b][B]")
     rc = load_library().simsd_commit_kv(_ptr(k_blk), _ptr(v_blk), _ptr(tau), _ptr(accept_len), _ptr(k_cache),
-                                        _ptr(v_cache), _ptr(cache_offsets), _ptr(cache_lens), b, B, Hkv, d,
-                                        flags, _ptr(status), _stream(stream))
+                                        _ptr(v_cache), _ptr(cache_offsets), _ptr(cache_lens), _ptr(pos),
+                                        _ptr(next_pos), b, B, Hkv, d, flags, _ptr(status), _stream(stream))
     _check("simsd_commit_kv", rc)

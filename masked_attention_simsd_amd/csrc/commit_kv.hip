@@ -7,6 +7,10 @@
 // order, to the end of the sequence's cache region, and its used length grows
 // by L_s.
 //
+// The same launch writes the positions the next round verifies (the block's
+// still-open positions, the rejected one first, then fresh ones), so a round
+// loop runs on the device without a host round trip.
+//
 // Pure data movement (a few KB per sequence, latency bound): one workgroup
 // per sequence. Wave 0 checks tau, inverts it in LDS and decides whether the
 // sequence can be committed; then every thread copies its 16-byte pieces of
@@ -15,6 +19,8 @@
 // used length. Only this workgroup reads or writes the sequence's length, so
 // the length array can be updated in place within the one launch.
 #include "simsd_internal.h"
+
+#include <climits>
 
 namespace simsd {
 
@@ -32,24 +38,53 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
   const int B = a.B;
 
   if (tid < 64) {
-    const int tv = lane < B ? a.tau[static_cast<size_t>(s) * B + lane] : 0;
+    const bool valid = lane < B;
+    const int tv = valid ? a.tau[static_cast<size_t>(s) * B + lane] : 0;
+    const int pv = (a.next_pos && valid) ? a.pos[static_cast<size_t>(s) * B + lane] : 0;
     const bool in_range = tv >= 1 && tv <= B;
     // a permutation of 1..B: every label in range and all B label bits present
-    unsigned long long bits = (lane < B && in_range) ? (1ull << (tv - 1)) : 0ull;
+    unsigned long long bits = (valid && in_range) ? (1ull << (tv - 1)) : 0ull;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) bits |= __shfl_xor(bits, o);
     const unsigned long long full = B == 64 ? ~0ull : ((1ull << B) - 1ull);
-    const bool perm = __ballot(lane < B && !in_range) == 0ull && bits == full;
-    if (perm && lane < B) inv[tv - 1] = lane;
-    if (lane == 0) {
-      const int L = a.accept_len[s], len = a.lens[s];
-      const int o0 = a.offsets[s], o1 = a.offsets[s + 1];
-      const int cap = o1 - o0;
-      // the region must lie inside the cache, and L more rows must fit after len
-      const bool region = o0 >= 0 && o1 >= o0 && o1 <= a.offsets[a.b];
-      const bool fits = region && L >= 0 && L <= B && len >= 0 && len <= cap && L <= cap - len;
-      sh_bits = !perm ? kDevBadTau : (!fits ? kDevCommitOverflow : 0);
-      sh_L = L, sh_len = len, sh_row0 = o0 + len;
+    const bool perm = __ballot(valid && !in_range) == 0ull && bits == full;
+    if (perm && valid) inv[tv - 1] = lane;
+    // the same values in every lane (one address each)
+    const int L = a.accept_len[s], len = a.lens[s];
+    const int o0 = a.offsets[s], o1 = a.offsets[s + 1];
+    const int cap = o1 - o0;
+    // the region must lie inside the cache, and L more rows must fit after len
+    const bool region = o0 >= 0 && o1 >= o0 && o1 <= a.offsets[a.b];
+    const bool fits = region && L >= 0 && L <= B && len >= 0 && len <= cap && L <= cap - len;
+    const int fail = !perm ? kDevBadTau : (!fits ? kDevCommitOverflow : 0);
+    if (lane == 0) sh_bits = fail, sh_L = L, sh_len = len, sh_row0 = o0 + len;
+    if (a.next_pos) {
+      // The next round's positions: the B smallest not in the cache. When L <
+      // B the rejected step's position comes first (its correction token is
+      // committed but has no key/value row yet), then the other open
+      // positions (label > L + 1) in increasing order (ties by pair index),
+      // then L positions following the block's largest. A sequence that
+      // commits nothing keeps its block.
+      int* nx = a.next_pos + static_cast<size_t>(s) * B;
+      int pmax = valid ? pv : INT_MIN;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) pmax = max(pmax, __shfl_xor(pmax, o));
+      const bool corr = valid && tv == L + 1;
+      const bool open = valid && tv > L + 1;
+      int rank = 0;
+      for (int t = 0; t < B; ++t) {
+        const int pt = __shfl(pv, t), tt = __shfl(tv, t);
+        rank += (tt > L + 1 && (pt < pv || (pt == pv && t < lane))) ? 1 : 0;
+      }
+      if (valid) {
+        if (fail) {
+          nx[lane] = pv;
+        } else {
+          if (corr) nx[0] = pv;
+          if (open) nx[(L < B ? 1 : 0) + rank] = pv;
+          if (lane < L) nx[B - L + lane] = pmax + 1 + lane;
+        }
+      }
     }
   }
   __syncthreads();

@@ -3,7 +3,9 @@
 // SimSD pages ([nl] "Technische Samenvatting: SimSD - Simple Speculative
 // Decoding in Diffusion Language Models" and [fr] "SimSD: Simple Speculative
 // Decoding in Diffusion Language Models", Methodologie 3): the mask slot D~_k
-// takes the rotary position of its paired data token D_k. The kernel makes
+// takes the rotary position of its paired data token D_k. The pair's
+// position is start + k, or given per pair (a later round of a block
+// re-verifies the positions still open, wherever they lie). The kernel makes
 // that literal: a workgroup owns response position k of one sequence (and a
 // chunk of heads), evaluates the d/2 rotation angles of that position once,
 // and applies the same angles to the rows of both D_k and D~_k, for query and
@@ -105,7 +107,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_copy_kernel(RopeArgs a, int
   // for the row (loads complete in issue order) and the fp64 angle evaluation
   // overlaps the row's latency.
   const double inv_freq = a.inv_freq[min(tid, half - 1)];
-  const long pos_d = static_cast<long>(a.start_pos[s]) + k;
+  // the pair's position: start + k, or its own entry of a [b][B] position array
+  const int pidx = a.positions ? s * a.B + k : s;
+  const long pos_d = static_cast<long>(a.start_pos[pidx]) + (a.positions ? 0 : k);
   // The two base pointers are pinned to scalar registers before the per-lane
   // select: selecting between the two argument slots instead would turn into a
   // per-lane load of the pointer itself, a full memory round trip before the

@@ -40,6 +40,13 @@ void fill_inv_freq(double* out, float base, int d) {
   for (int i = 0; i < d / 2; ++i) out[i] = std::pow(static_cast<double>(base), -2.0 * i / d);
 }
 
+// RoPE flags: known bits only; explicit positions exclude the no-copy
+// ablation (which numbers the mask slots after a consecutive data section).
+bool rope_flags_ok(uint32_t f) {
+  if (f & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY | SIMSD_ROPE_POSITIONS)) return false;
+  return !((f & SIMSD_ROPE_NO_COPY) && (f & SIMSD_ROPE_POSITIONS));
+}
+
 int check_common(int b, int B, int Hq, int Hkv, int d) {
   if (b < 1 || B < 1 || B > 64 || Hq < 1 || Hkv < 1) return SIMSD_ERR_SIZE;
   if (Hq % Hkv != 0) return SIMSD_ERR_HEADS;
@@ -76,7 +83,7 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
     return SIMSD_ERR_ALIGN;
   if (rope) {
     if (!rope->start_pos) return SIMSD_ERR_NULL;
-    if (rope->flags & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY)) return SIMSD_ERR_FLAGS;
+    if (!rope_flags_ok(rope->flags)) return SIMSD_ERR_FLAGS;
     if (!(rope->base > 0.0f) || !std::isfinite(rope->base)) return SIMSD_ERR_SCALE;
     // the cos/sin table lives in LDS beside the key ring
     const long npos = (rope->flags & SIMSD_ROPE_NO_COPY) ? 2L * B : B;
@@ -143,6 +150,7 @@ int verify_attention_impl(const void* q_blk, const void* k_blk, const void* v_bl
     fill_inv_freq(a.rope_inv_freq, rope->base, d);
     a.rope_interleaved = (rope->flags & SIMSD_ROPE_INTERLEAVED) ? 1 : 0;
     a.rope_no_copy = (rope->flags & SIMSD_ROPE_NO_COPY) ? 1 : 0;
+    a.rope_positions = (rope->flags & SIMSD_ROPE_POSITIONS) ? 1 : 0;
     a.k_rot = static_cast<uint16_t*>(rope->k_rot);
   }
   return launch_status(simsd::launch_verify_attention(a, plan, static_cast<hipStream_t>(stream)));
@@ -212,7 +220,7 @@ int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, i
   if (!q_blk || !k_blk || !start_pos) return SIMSD_ERR_NULL;
   int rc = check_common(b, B, Hq, Hkv, d);
   if (rc) return rc;
-  if (flags & ~(SIMSD_ROPE_INTERLEAVED | SIMSD_ROPE_NO_COPY)) return SIMSD_ERR_FLAGS;
+  if (!rope_flags_ok(flags)) return SIMSD_ERR_FLAGS;
   if (!(rope_base > 0.0f) || !std::isfinite(rope_base)) return SIMSD_ERR_SCALE;
   if (!aligned16(q_blk) || !aligned16(k_blk)) return SIMSD_ERR_ALIGN;
   simsd::RopeArgs a{};
@@ -223,6 +231,7 @@ int simsd_rope_copy(void* q_blk, void* k_blk, const int32_t* start_pos, int b, i
   fill_inv_freq(a.inv_freq, rope_base, d);
   a.interleaved = (flags & SIMSD_ROPE_INTERLEAVED) ? 1 : 0;
   a.no_copy = (flags & SIMSD_ROPE_NO_COPY) ? 1 : 0;
+  a.positions = (flags & SIMSD_ROPE_POSITIONS) ? 1 : 0;
   return launch_status(simsd::launch_rope_copy(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -435,16 +444,16 @@ int simsd_accept_logits(const float* target_logits, const float* draft_logits, f
 }
 
 int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, const int32_t* accept_len,
-                    void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens, int b,
-                    int B, int Hkv, int d, uint32_t flags, int32_t* status, void* stream) {
+                    void* k_cache, void* v_cache, const int32_t* cache_offsets, int32_t* cache_lens,
+                    const int32_t* pos, int32_t* next_pos, int b, int B, int Hkv, int d, uint32_t flags,
+                    int32_t* status, void* stream) {
   if (!k_blk || !v_blk || !tau || !accept_len || !k_cache || !v_cache || !cache_offsets || !cache_lens)
     return SIMSD_ERR_NULL;
+  if (next_pos && !pos) return SIMSD_ERR_NULL;
   int rc = check_common(b, B, Hkv, Hkv, d);
   if (rc) return rc;
   if (flags & ~(SIMSD_KV_HEAD_MAJOR | SIMSD_KV_PAIRED)) return SIMSD_ERR_FLAGS;
   if (!paired_ok(flags, k_cache, v_cache, d)) return SIMSD_ERR_FLAGS;
-  if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
-    return SIMSD_ERR_ALIGN;
   // each workgroup rewrites its sequence's length after reading its inputs:
   // the lengths must not be one of the inputs another workgroup reads (the
   // cache and the block are the caller's to keep apart)
@@ -456,6 +465,17 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
   if (overlap(cache_lens, nl, tau, nl * B) || overlap(cache_lens, nl, accept_len, nl) ||
       overlap(cache_lens, nl, cache_offsets, nl + 4))
     return SIMSD_ERR_ALIAS;
+  // next_pos is written by the workgroup of its sequence after that workgroup
+  // read the sequence's inputs: it may be pos itself, but no other input
+  if (next_pos) {
+    const size_t np = nl * B;
+    if ((next_pos != pos && overlap(next_pos, np, pos, np)) || overlap(next_pos, np, tau, np) ||
+        overlap(next_pos, np, accept_len, nl) || overlap(next_pos, np, cache_offsets, nl + 4) ||
+        overlap(next_pos, np, cache_lens, nl))
+      return SIMSD_ERR_ALIAS;
+  }
+  if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache))
+    return SIMSD_ERR_ALIGN;
   simsd::CommitArgs a{};
   a.k_blk = static_cast<const uint16_t*>(k_blk);
   a.v_blk = static_cast<const uint16_t*>(v_blk);
@@ -465,6 +485,8 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
   a.v_cache = static_cast<uint16_t*>(v_cache);
   a.offsets = cache_offsets;
   a.lens = cache_lens;
+  a.pos = pos;
+  a.next_pos = next_pos;
   a.status = status;
   a.b = b, a.B = B, a.Hkv = Hkv, a.d = d;
   a.head_major = (flags & SIMSD_KV_HEAD_MAJOR) ? 1 : 0;

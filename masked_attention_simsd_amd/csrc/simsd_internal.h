@@ -66,9 +66,10 @@ __device__ __forceinline__ void rope_rotate(uint16_t xa, uint16_t xb, double co,
 struct RopeArgs {
   uint16_t* q;
   uint16_t* k;
-  const int32_t* start_pos;
+  const int32_t* start_pos;  // [b] (pair k at start_pos[s] + k), or [b][B] positions
   int b, B, Hq, Hkv, d;
   int interleaved, no_copy;
+  int positions;  // 1: start_pos holds one position per pair ([b][B])
   double inv_freq[kMaxRopeFreqs];  // base^(-2i/d), i < d/2
 };
 
@@ -107,8 +108,8 @@ struct AttnArgs {
   // RoPE-copy fused into the prologue (rope != 0): query rows and block key
   // rows are rotated on the fly; the rotated block keys go to k_rot if set
   int rope;
-  const int32_t* start_pos;
-  int rope_interleaved, rope_no_copy;
+  const int32_t* start_pos;  // [b], or [b][B] positions with rope_positions
+  int rope_interleaved, rope_no_copy, rope_positions;
   uint16_t* k_rot;
   double rope_inv_freq[kMaxRopeFreqs];  // base^(-2i/d), i < d/2
   // explicit block mask (mask_mode): bit c of word c/64 of row r's
@@ -133,6 +134,8 @@ struct CommitArgs {
   uint16_t* v_cache;
   const int32_t* offsets;  // [b+1] region bounds
   int32_t* lens;           // [b] used rows, updated in place
+  const int32_t* pos;      // [b][B] positions of this round's pairs (with next_pos)
+  int32_t* next_pos;       // [b][B] positions of the next round, or null
   int32_t* status;
   int b, B, Hkv, d;
   int head_major;

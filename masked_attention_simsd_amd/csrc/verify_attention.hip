@@ -263,6 +263,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE_B];
   __shared__ float xml[KS == 2 ? NWC * QB * 64 * 2 : 1];  // (m, l) handed between key slices
   __shared__ int tau_s[64];
+  __shared__ int pos_s[ROPE ? 64 : 1];  // fused RoPE with a position per pair
   __shared__ int last_s;
   extern __shared__ double rope_tab[];  // ROPE: [position][d/2] x (cos, sin), rows padded
 
@@ -316,7 +317,9 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   int P = a.prefix_lens[s] - (a.prefix_lens_are_ends ? o0 : 0);
   // read before the first DMA is issued, so it can be a scalar load (the DMA
   // asm clobbers memory as far as the compiler knows)
-  const long pos0 = ROPE ? static_cast<long>(a.start_pos[s]) : 0;
+  // (with a position per pair the table reads them from LDS, staged below;
+  // this then loads the sequence's first one, unused)
+  const long pos0 = ROPE ? static_cast<long>(a.start_pos[a.rope_positions ? s * a.B : s]) : 0;
   const int rows_total = a.offsets[a.b];  // rows of a head-major cache per KV head
 
   // ---- tau, the workgroup's query rows (and the RoPE frequencies) ----
@@ -368,6 +371,13 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
         const int* tau_row = a.tau + static_cast<size_t>(s) * B;
         dma4(tau_row, 4u * static_cast<uint32_t>(min(lane, B - 1)),
              static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIMSD_LDS int*)tau_s)));
+      }
+      if constexpr (ROPE) {
+        if (a.rope_positions) {
+          const int* pos_row = a.start_pos + static_cast<size_t>(s) * B;
+          dma4(pos_row, 4u * static_cast<uint32_t>(min(lane, B - 1)),
+               static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIMSD_LDS int*)pos_s)));
+        }
       }
     }
     const uint16_t* q_seq = a.q_blk + static_cast<size_t>(s) * twoB * a.Hq * D;
@@ -531,15 +541,17 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   if constexpr (ROPE) {
     // cos/sin of every (block position, frequency) this workgroup needs,
     // computed while the first tiles are in flight. Row p of the table is
-    // position start + p: the B data positions, then (without the copy rule)
-    // the B positions after them that the mask slots take instead. Entry e of
+    // position start + p (or pair p's own position): the B data positions,
+    // then (without the copy rule) the B positions after them that the mask
+    // slots take instead. Entry e of
     // the table has frequency e % (D/2) = lane % (D/2), read from the staged
     // frequencies.
     const double inv_l = rope_freq[lane % (D / 2)];
     static_assert((NW * 64) % (D / 2) == 0, "table entries keep the lane's frequency");
     for (int e = tid; e < rope_npos * (D / 2); e += NW * 64) {
       const int pi = e / (D / 2);
-      const double ang = static_cast<double>(pos0 + pi) * inv_l;
+      const long pos = a.rope_positions ? static_cast<long>(pos_s[pi]) : pos0 + pi;
+      const double ang = static_cast<double>(pos) * inv_l;
       double sn, cs;
       sincos(ang, &sn, &cs);
       const int f = e - pi * (D / 2);  // frequency index

@@ -1,6 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point
 declared in include/simsd.h, and rejects bad arguments on the host before any
-launch (every call below returns before touching the HIP runtime)."""
+launch. Every call below returns before touching the HIP runtime: a case that
+must pass a check stops at a later one (a missing workspace, a misaligned
+pointer), so no call with these fake pointers ever reaches a launch."""
 import ctypes
 import os
 import re
@@ -14,6 +16,17 @@ HEADER = os.path.join(ROOT, "include", "simsd.h")
 
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced on these paths
 MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+@pytest.fixture(autouse=True)
+def no_launch_attempted():
+    """Fails a test in which any call got as far as a kernel launch (on a
+    machine without a GPU the launch fails and records its HIP error)."""
+    ok = os.path.exists(binding.LIB_PATH)
+    before = binding.load_library().simsd_last_hip_error() if ok else 0
+    yield
+    if ok:
+        assert binding.load_library().simsd_last_hip_error() == before == 0, "a call reached a kernel launch"
 
 
 def _declared():
@@ -91,17 +104,19 @@ def _attn_rope(lib, **kw):
 def test_fused_rope_attention_host_errors(lib):
     assert _attn_rope(lib, sp=None) == 1
     assert _attn_rope(lib, q=None) == 1
-    assert _attn_rope(lib, rflags=4) == 5
+    assert _attn_rope(lib, rflags=8) == 5
+    assert _attn_rope(lib, rflags=6) == 5  # explicit positions exclude the no-copy ablation
+    assert _attn_rope(lib, rflags=4, ws=None) == 6  # accepted: stops at the workspace, the last check
     assert _attn_rope(lib, flags=3) == 5
     assert _attn_rope(lib, base=0.0) == 9
     assert _attn_rope(lib, base=float("nan")) == 9
     assert _attn_rope(lib, krot=MISALIGNED) == 7
     # the cos/sin table: (NO_COPY ? 2B : B) * d <= 8192
     assert _attn_rope(lib, B=33, rflags=2) == 2
-    assert _attn_rope(lib, B=64, rflags=2, d=64, Hq=8, Hkv=2) != 2
+    assert _attn_rope(lib, B=64, rflags=2, d=64, Hq=8, Hkv=2, ws=None) == 6
     # k_rot overlapping k_blk: [b][2B][Hkv][d] bf16 = 2*8*2*128*2 bytes
     assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 4096)) == 10
-    assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 8192)) != 10
+    assert _attn_rope(lib, krot=ctypes.c_void_p(0x100000 + 8192), ws=None) == 6
     assert lib.simsd_status_string(10)
 
 
@@ -178,7 +193,9 @@ def test_rope_host_errors(lib):
     assert f(B=65) == 2
     assert f(Hq=7) == 3
     assert f(d=32) == 4
-    assert f(flags=4) == 5
+    assert f(flags=8) == 5
+    assert f(flags=6) == 5  # explicit positions exclude the no-copy ablation
+    assert f(flags=4, k=MISALIGNED) == 7  # positions accepted: stops at the alignment check
     assert f(base=0.0) == 9
     assert f(base=float("inf")) == 9
     assert f(k=MISALIGNED) == 7
@@ -243,11 +260,12 @@ def test_attention_mask_host_errors(lib):
 def test_commit_kv_host_errors(lib):
     def f(**kw):
         a = dict(k=FAKE, v=FAKE, tau=ctypes.c_void_p(0x200000), L=ctypes.c_void_p(0x300000), kc=FAKE, vc=FAKE,
-                 off=ctypes.c_void_p(0x400000), lens=ctypes.c_void_p(0x400040), b=4, B=8, Hkv=2, d=128,
-                 flags=0, status=None)
+                 off=ctypes.c_void_p(0x400000), lens=ctypes.c_void_p(0x400040), pos=None, nxt=None, b=4, B=8,
+                 Hkv=2, d=128, flags=0, status=None)
         a.update(kw)
         return lib.simsd_commit_kv(a["k"], a["v"], a["tau"], a["L"], a["kc"], a["vc"], a["off"], a["lens"],
-                                   a["b"], a["B"], a["Hkv"], a["d"], a["flags"], a["status"], None)
+                                   a["pos"], a["nxt"], a["b"], a["B"], a["Hkv"], a["d"], a["flags"], a["status"],
+                                   None)
     for name in ("k", "v", "tau", "L", "kc", "vc", "off", "lens"):
         assert f(**{name: None}) == 1, name
     assert f(b=0) == 2
@@ -263,3 +281,13 @@ def test_commit_kv_host_errors(lib):
     assert f(lens=ctypes.c_void_p(0x200010)) == 10
     assert f(lens=ctypes.c_void_p(0x300000)) == 10
     assert f(lens=ctypes.c_void_p(0x400008)) == 10  # inside cache_offsets
+    # next positions need this round's positions, may overwrite them in place,
+    # and may not overlap any other input ([b][B] int32 = 128 bytes here)
+    P0, N0 = ctypes.c_void_p(0x500000), ctypes.c_void_p(0x600000)
+    assert f(nxt=N0) == 1
+    # accepted: these stop at the alignment check, which follows the aliasing one
+    assert f(pos=P0, nxt=N0, k=MISALIGNED) == 7
+    assert f(pos=P0, nxt=P0, k=MISALIGNED) == 7
+    assert f(pos=P0, nxt=ctypes.c_void_p(0x500040)) == 10
+    assert f(pos=P0, nxt=ctypes.c_void_p(0x200040)) == 10  # over tau
+    assert f(pos=P0, nxt=ctypes.c_void_p(0x3FFFF0)) == 10  # over cache_offsets

@@ -45,17 +45,32 @@ def test_commit_matches_oracle(shape):
         tau[1, 0] = tau[1, -1] if B > 1 else 2  # not a permutation
         L[2] = B  # may overflow its region
     ek, ev, el, est = oracle.commit_kv(f64(kb), f64(vb), tau, L, f64(kc), f64(vc), off, lens, head_major)
+    # this round's positions: scattered, unordered, distinct per sequence
+    pos = np.stack([rng.choice(100000, size=B, replace=False) for _ in range(b)]).astype(np.int32)
+    enext = oracle.next_positions(pos, tau, L)
+    enext[est != 0] = pos[est != 0]  # a sequence that commits nothing keeps its block
     ext = torch.tensor(np.concatenate([off, lens]), dtype=torch.int32, device="cuda")
     status = torch.zeros(b, dtype=torch.int32, device="cuda")
     gk, gv = kc.cuda(), vc.cuda()
+    gpos = torch.from_numpy(pos).cuda()
+    gnext = torch.full_like(gpos, -7)
     binding.simsd_commit_kv(kb.cuda(), vb.cuda(), torch.from_numpy(tau).cuda(), torch.from_numpy(L).cuda(),
-                            gk, gv, ext[:b + 1], ext[b + 1:],
+                            gk, gv, ext[:b + 1], ext[b + 1:], pos=gpos, next_pos=gnext,
                             flags=binding.SIMSD_KV_HEAD_MAJOR if head_major else 0, status=status)
     torch.cuda.synchronize()
     say(f"  L {L.tolist()} status {status.cpu().tolist()} lens {ext[b + 1:].cpu().tolist()}")
     assert np.array_equal(ext[b + 1:].cpu().numpy(), el)
     assert np.array_equal(status.cpu().numpy(), est)
     assert np.array_equal(f64(gk), ek) and np.array_equal(f64(gv), ev)
+    assert np.array_equal(gnext.cpu().numpy(), enext)
+    # in place: next_pos may be pos itself
+    kc2, vc2 = kc.cuda(), vc.cuda()
+    ext2 = torch.tensor(np.concatenate([off, lens]), dtype=torch.int32, device="cuda")
+    binding.simsd_commit_kv(kb.cuda(), vb.cuda(), torch.from_numpy(tau).cuda(), torch.from_numpy(L).cuda(),
+                            kc2, vc2, ext2[:b + 1], ext2[b + 1:], pos=gpos, next_pos=gpos,
+                            flags=binding.SIMSD_KV_HEAD_MAJOR if head_major else 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpos.cpu().numpy(), enext)
 
 
 def grown_cache(x, caps, head_major, fill=NAN_BF16):
@@ -139,7 +154,13 @@ def test_lengths_past_the_region_are_flagged_and_clamped():
 
 @pytest.mark.parametrize("head_major", [True, False])
 def test_rounds_follow_the_oracle_chain(head_major):
-    rounds, b, Hq, Hkv, d, B, V = 3, 4, 8, 2, 128, 8, 256
+    # Rounds of RoPE-copy (explicit positions) -> attention over the grown
+    # cache -> acceptance -> commit, the positions of each round written by the
+    # previous commit on the device. After a rejection the committed
+    # correction token enters the next round as the data token of the first
+    # pair (the rejected position) at temporal step 1, with draft probability
+    # equal to the target's, so it is accepted and its key/value row committed.
+    rounds, b, Hq, Hkv, d, B, V = 4, 8, 8, 2, 128, 8, 256
     say(f"{rounds} rounds, head_major={head_major}")
     w0 = synth.custom(b=b, Hq=Hq, Hkv=Hkv, d=d, B=B, V=V, prefix=(40, 400))
     x0 = synth.make_inputs(w0, with_accept=False, seed=40)
@@ -147,43 +168,75 @@ def test_rounds_follow_the_oracle_chain(head_major):
     caps = lens0 + rounds * B
     k, v, roff, lens = grown_cache(x0, caps, head_major, fill=0.0)
     fl = binding.SIMSD_KV_HEAD_MAJOR if head_major else 0
-    # device state: cache and one [2b+1] array (bounds, then lengths = start positions)
+    # device state: cache, one [2b+1] array (bounds, then lengths), positions
     gk, gv = k.cuda(), v.cuda()
     ext = torch.tensor(np.concatenate([roff, lens]), dtype=torch.int32, device="cuda")
     glens = ext[b + 1:]
+    gpos = torch.from_numpy((lens0[:, None] + np.arange(B)[None, :]).astype(np.int32)).cuda()
     # oracle state (fp64 copies of the same bf16 values)
     ok_, ov_, olens = f64(k), f64(v), lens.copy()
+    opos = gpos.cpu().numpy()
+    cached = [[] for _ in range(b)]  # positions committed after the prompt
     maxp = int(caps.max())
+    prev_L = prev_corr = None
+    partial = 0  # rounds of a sequence with tau != identity and 0 < L < B
     for r in range(rounds):
-        x = synth.make_inputs(w0, seed=41 + r)  # this round's block, drafts and target / draft probabilities
-        qg, kg = x["q_blk"].cuda(), x["k_blk"].cuda()
-        vg, tg = x["v_blk"].cuda(), x["tau"].cuda()
-        binding.simsd_rope_copy(qg, kg, glens, w0.rope_base)
+        x = synth.make_inputs(w0, seed=41 + r)  # this round's block, drafts and probabilities
+        tau, draft, q, p = x["tau"].clone(), x["draft"].clone(), x["q"].clone(), x["p"]
+        if r > 0:
+            for s in range(b):
+                if prev_L[s] < B:
+                    j = int((tau[s] == 1).nonzero()[0, 0])
+                    tau[s, j], tau[s, 0] = tau[s, 0].clone(), 1
+                    draft[s, 0] = int(prev_corr[s])
+                    q[s, 0] = p[s, 0]
+        qg, kg, vg, tg = x["q_blk"].cuda(), x["k_blk"].cuda(), x["v_blk"].cuda(), tau.cuda()
+        binding.simsd_rope_copy(qg, kg, gpos, w0.rope_base, binding.SIMSD_ROPE_POSITIONS)
         out = binding.simsd_verify_attention(qg, kg, vg, gk, gv, ext, tg, max_prefix=maxp,
                                              flags=fl | binding.SIMSD_PREFIX_LENS | binding.SIMSD_OUT_F32)
-        L, corr = binding.simsd_accept(x["p"].cuda(), x["q"].cuda(), x["draft"].cuda(), tg, x["u"].cuda())
+        L, corr = binding.simsd_accept(p.cuda(), q.cuda(), draft.cuda(), tg, x["u"].cuda())
         status = torch.zeros(b, dtype=torch.int32, device="cuda")
-        binding.simsd_commit_kv(kg, vg, tg, L, gk, gv, ext[:b + 1], glens, flags=fl, status=status)
+        gnext = torch.empty_like(gpos)
+        binding.simsd_commit_kv(kg, vg, tg, L, gk, gv, ext[:b + 1], glens, pos=gpos, next_pos=gnext,
+                                flags=fl, status=status)
         torch.cuda.synchronize()
 
-        q_r = bf16_round(oracle.rope_copy(f64(x["q_blk"]), olens, w0.rope_base))
-        k_r = bf16_round(oracle.rope_copy(f64(x["k_blk"]), olens, w0.rope_base))
+        tn = tau.numpy()
+        q_r = bf16_round(oracle.rope_copy(f64(x["q_blk"]), opos, w0.rope_base))
+        k_r = bf16_round(oracle.rope_copy(f64(x["k_blk"]), opos, w0.rope_base))
         kp, po = oracle.pack_regions(ok_, roff, olens, head_major)
         vp, _ = oracle.pack_regions(ov_, roff, olens, head_major)
         if head_major:
             kp, vp = kp.transpose(1, 0, 2), vp.transpose(1, 0, 2)
-        ref, _ = oracle.verify_attention(q_r, k_r, f64(x["v_blk"]), kp, vp, po, x["tau"].numpy(),
-                                         threads=ORACLE_THREADS)
-        acc = oracle.accept(x["p"].numpy(), x["q"].numpy(), x["draft"].numpy(), x["tau"].numpy(), x["u"].numpy())
-        ok_, ov_, olens, ost = oracle.commit_kv(k_r, f64(x["v_blk"]), x["tau"].numpy(), acc["accept_len"], ok_,
-                                                ov_, roff, olens, head_major)
+        ref, _ = oracle.verify_attention(q_r, k_r, f64(x["v_blk"]), kp, vp, po, tn, threads=ORACLE_THREADS)
+        acc = oracle.accept(p.numpy(), q.numpy(), draft.numpy(), tn, x["u"].numpy())
+        ok_, ov_, olens, ost = oracle.commit_kv(k_r, f64(x["v_blk"]), tn, acc["accept_len"], ok_, ov_, roff,
+                                                olens, head_major)
+        onext = oracle.next_positions(opos, tn, acc["accept_len"])
+        done = oracle.committed_positions(opos, tn, acc["accept_len"])
         err = float(np.abs(f64(out) - ref).max())
-        say(f"  round {r}: attention max-abs {err:.3e}, accepted {L.cpu().tolist()}, lens {glens.cpu().tolist()}")
+        Lh, ch = L.cpu().numpy(), corr.cpu().numpy()
+        say(f"  round {r}: attention max-abs {err:.3e}, accepted {Lh.tolist()}, lens {glens.cpu().tolist()}")
         assert err <= 4e-3
-        assert np.array_equal(L.cpu().numpy(), acc["accept_len"])
+        assert np.array_equal(Lh, acc["accept_len"])
+        assert not ((ch != acc["correction"]) & (acc["boundary"] == 0)).any()
         assert status.cpu().tolist() == [0] * b and ost.tolist() == [0] * b
         assert np.array_equal(glens.cpu().numpy(), olens)
         # values are copied bit for bit; keys carry the RoPE-copy result (within 1 bf16 ulp of the oracle's)
         assert np.array_equal(f64(gv), ov_)
-        kd = f64(gk)
-        assert (np.abs(kd - ok_) <= bf16_ulp(ok_)).all()
+        assert (np.abs(f64(gk) - ok_) <= bf16_ulp(ok_)).all()
+        nx = gnext.cpu().numpy()
+        assert np.array_equal(nx, onext)
+        for s in range(b):
+            if r > 0 and prev_L[s] < B:
+                assert Lh[s] >= 1, "the committed correction token was not accepted"
+            cached[s] += done[s]
+            seen = cached[s] + nx[s].tolist()
+            # committed plus next-round positions: each once, no gap after the prompt
+            assert len(seen) == len(set(seen)) and sorted(seen) == list(range(lens0[s], max(seen) + 1)), s
+            if 0 < Lh[s] < B and not (tn[s] == np.arange(1, B + 1)).all():
+                partial += 1
+        prev_L, prev_corr = Lh, ch
+        gpos, opos = gnext, onext
+    say(f"  rounds with tau != identity and 0 < L < B: {partial}")
+    assert partial >= 4

@@ -55,6 +55,12 @@ CASES = [
     (1, 4, 1, 64, 64, (130, 130), binding.SIMSD_ROPE_NO_COPY, binding.SIMSD_OUT_F32),
     (1, 32, 8, 128, 64, (300, 300), 0, binding.SIMSD_KV_HEAD_MAJOR),
     (1, 8, 2, 128, 32, (500, 500), binding.SIMSD_ROPE_NO_COPY, 0),
+    # a position per pair (a later round of a block)
+    (3, 8, 2, 128, 8, (100, 700), binding.SIMSD_ROPE_POSITIONS, 0),
+    (2, 32, 8, 128, 16, (1000, 2500), binding.SIMSD_ROPE_POSITIONS | binding.SIMSD_ROPE_INTERLEAVED,
+     binding.SIMSD_KV_HEAD_MAJOR | binding.SIMSD_OUT_F32),
+    (2, 32, 8, 128, 8, (0, 3000), binding.SIMSD_ROPE_POSITIONS, binding.SIMSD_DATA_SKIP),
+    (1, 32, 8, 128, 40, (300, 300), binding.SIMSD_ROPE_POSITIONS, 0),
 ]
 
 
@@ -76,6 +82,11 @@ def test_fused_equals_two_calls_bit_exact(case):
     x = synth.make_inputs(w, with_accept=False, seed=hash(case) % 1000)
     # positions far from 0 (the rotation matters) and different per sequence
     x["start_pos"] = x["start_pos"] + torch.arange(b, dtype=torch.int32) * 977 + 50000
+    if rflags & binding.SIMSD_ROPE_POSITIONS:
+        # one position per pair, scattered and unordered
+        gen = torch.Generator().manual_seed(B)
+        x["start_pos"] = torch.stack([torch.randperm(4 * B, generator=gen)[:B] * 37 + int(p0)
+                                      for p0 in x["start_pos"]]).to(torch.int32).contiguous()
     g = prep(x, flags & binding.SIMSD_KV_HEAD_MAJOR)
     q0, k0 = g["q_blk"].clone(), g["k_blk"].clone()
     mp = int(pre[1])
