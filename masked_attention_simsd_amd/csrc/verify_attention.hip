@@ -264,6 +264,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   __shared__ float xml[KS == 2 ? NWC * QB * 64 * 2 : 1];  // (m, l) handed between key slices
   __shared__ int tau_s[64];
   __shared__ int pos_s[ROPE ? 64 : 1];  // fused RoPE with a position per pair
+  __shared__ int vbad_s;                // a block V row held a non-finite value (split 0)
   __shared__ int last_s;
   extern __shared__ double rope_tab[];  // ROPE: [position][d/2] x (cos, sin), rows padded
 
@@ -519,6 +520,7 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   } else {
     if (tid < 64) tau_s[tid] = tau_ld;
   }
+  if (tid == 0) vbad_s = 0;
   wait_lgkm0();
   block_barrier();  // tau_s, the query rows (and the RoPE frequencies) visible
   if constexpr (QDMA) {
@@ -758,6 +760,34 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
   // LDS and tile t-1 is consumed), then refill the slot tile t-1 used.
   auto advance = [&](int t) {
     wait_tile<DPW, NS - 2>(min(NS - 2, ntiles - 1 - t));
+    if (t < n_blk) {
+      // A block tile: every lane zeroes the non-finite values of the 16-byte
+      // V pieces it brought in itself (landed with this wave's wait), before
+      // the barrier publishes the tile. A hidden key's zero weight then never
+      // meets a NaN or Inf in the product (0 * NaN would be NaN); the terms of
+      // visible keys are added back after the loop.
+      const uint32_t vstage = static_cast<uint32_t>((t % NS) * STAGE_B + TENSOR_B);
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        SIMSD_LDS u32x4* pc =
+            reinterpret_cast<SIMSD_LDS u32x4*>(ring_l + vstage + (i * NW + wave) * 1024 + 16 * lane);
+        const u32x4 x = *pc;
+        u32x4 y;
+        bool bad = false;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = x[w] & 0xffffu, hi = x[w] >> 16;
+          const bool bl = (lo & 0x7f80u) == 0x7f80u, bh = (hi & 0x7f80u) == 0x7f80u;
+          y[w] = (bl ? 0u : lo) | (bh ? 0u : (hi << 16));
+          bad = bad || bl || bh;
+        }
+        if (bad) *pc = y;
+        found = found || bad;
+      }
+      if (found) vbad_s = 1;
+      wait_lgkm0();
+    }
     block_barrier();
     if (t + NS - 1 < ntiles) issue(t + NS - 1);
   };
@@ -860,6 +890,52 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
                          *reinterpret_cast<const f32x4*>(xo + ((rw * QB + qb) * DB + db) * 256 + 4 * lane) * wb;
         m_run[qb] = m_new;
       }
+    }
+  }
+
+  // ---- split 0: the non-finite block values its rows see ----
+  // Rare (only when a block V row held a NaN or Inf; uniform): for every
+  // block key its query sees, each owner lane folds the non-finite values at
+  // its d columns into the IEEE sum they form (NaN, +Inf or -Inf) and adds it
+  // to its unnormalised output, as the plain softmax over the allowed keys
+  // would (every allowed key has a positive weight there).
+  if (split == 0 && owner && __builtin_amdgcn_readfirstlane(vbad_s)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      uint32_t pos_inf[DB], neg_inf[DB], nan_bits[DB];  // bit i: column 16 db + 4 a16 + i
+#pragma unroll
+      for (int db = 0; db < DB; ++db) pos_inf[db] = neg_inf[db] = nan_bits[db] = 0u;
+#pragma unroll 1
+      for (int c = 0; c < twoB; ++c) {
+        bool ok;
+        if constexpr (MASK)
+          ok = (((c >= 64 ? mhi[qb] : mlo[qb]) >> (c & 63)) & 1ull) != 0;
+        else
+          ok = block_allowed(slot_q[qb], tau_q[qb], c >= B, tau_s[c >= B ? c - B : c], a.data_rule);
+        if (!ok) continue;
+        const char* vr = vblk + static_cast<size_t>(c) * rsb_blk + 8 * a16;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint2 v4 = *reinterpret_cast<const uint2*>(vr + 32 * db);
+          const uint32_t e[4] = {v4.x & 0xffffu, v4.x >> 16, v4.y & 0xffffu, v4.y >> 16};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool inf = (e[i] & 0x7fffu) == 0x7f80u, nan = (e[i] & 0x7fffu) > 0x7f80u;
+            pos_inf[db] |= (inf && !(e[i] & 0x8000u)) ? (1u << i) : 0u;
+            neg_inf[db] |= (inf && (e[i] & 0x8000u)) ? (1u << i) : 0u;
+            nan_bits[db] |= nan ? (1u << i) : 0u;
+          }
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool pi = (pos_inf[db] >> i) & 1u, ni = (neg_inf[db] >> i) & 1u, na = (nan_bits[db] >> i) & 1u;
+          if (na || (pi && ni)) oacc[qb][db][i] = __builtin_nanf("");
+          else if (pi) oacc[qb][db][i] += INFINITY;
+          else if (ni) oacc[qb][db][i] -= INFINITY;
+        }
     }
   }
 

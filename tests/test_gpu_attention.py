@@ -154,6 +154,47 @@ def test_hidden_keys_do_not_change_slot_rows_bit_exact():
             assert torch.equal(out[s, 8 + i], base[s, 8 + i]), (s, i)
 
 
+@pytest.mark.parametrize("value", [float("nan"), float("inf"), float("-inf")], ids=["nan", "inf", "-inf"])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 128, 8, 300), (1, 32, 8, 128, 16, 600), (2, 4, 1, 64, 5, 90)],
+                         ids=["b2_B8", "b1_B16_128rows", "d64_B5"])
+def test_non_finite_hidden_keys_do_not_change_slot_rows(shape, value):
+    # NaN or Inf in the key AND value rows of every block key a mask slot may
+    # not see leave that slot's output and lse bit-identical; a mask slot that
+    # sees such a value propagates it exactly as the oracle's plain softmax
+    b, Hq, Hkv, d, B, P = shape
+    say(f"non-finite hidden keys {shape} value {value}")
+    w = synth.custom(b=b, Hq=Hq, Hkv=Hkv, d=d, B=B, prefix=(P, P))
+    x = synth.make_inputs(w, with_accept=False, seed=78)
+    fl = binding.SIMSD_OUT_F32
+    base, base_lse = run_gpu(x, flags=fl)
+    tau = x["tau"]
+    for s in range(b):
+        for i in range(B):
+            y = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in x.items()}
+            hidden_d = [j for j in range(B) if tau[s, j] >= tau[s, i]]
+            hidden_t = [B + j for j in range(B) if tau[s, j] < tau[s, i]]
+            for c in hidden_d + hidden_t:
+                y["k_blk"][s, c] = value
+                y["v_blk"][s, c] = value
+            out, lse = run_gpu(y, flags=fl)
+            assert torch.equal(out[s, B + i], base[s, B + i]), (s, i)
+            assert torch.equal(lse[s, B + i], base_lse[s, B + i]), (s, i)
+            # every other sequence is untouched
+            others = [t for t in range(b) if t != s]
+            assert torch.equal(out[others], base[others])
+    # visible: a value vector of one data token with a NaN / Inf entry reaches
+    # exactly the rows that see that token, as in the oracle
+    y = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in x.items()}
+    j = int((tau[0] == 1).nonzero()[0, 0])  # step 1: seen by every later mask slot
+    y["v_blk"][0, j, :, 3] = value
+    out, lse = run_gpu(y, flags=fl)
+    ref, ref_lse = run_oracle(y)
+    o, r = out.cpu().double().numpy(), ref
+    assert np.array_equal(np.isnan(o), np.isnan(r)) and np.array_equal(np.isinf(o), np.isinf(r))
+    fin = np.isfinite(r)
+    assert np.abs(o[fin] - r[fin]).max() <= TOL_F32
+
+
 def test_deterministic_and_split_independent():
     x = inputs("b8")
     a, _ = run_gpu(x, flags=binding.SIMSD_OUT_F32)
