@@ -115,15 +115,13 @@ _WORKLOAD_REFS = {}  # oracle results per (workload, sequences): the layout does
 @pytest.mark.parametrize("layout", [0, binding.SIMSD_KV_HEAD_MAJOR,
                                     binding.SIMSD_KV_HEAD_MAJOR | binding.SIMSD_KV_PAIRED],
                          ids=["token_major", "head_major", "paired_head_major"])
-@pytest.mark.parametrize("cfg,seqs", [("tiny", None), ("b4", None), ("b8", None),
-                                      ("b16", [0, 5]), ("ragged", None)])
+@pytest.mark.parametrize("cfg,seqs", [("tiny", None), ("b4", None), ("b8", None), ("b16", None), ("ragged", None)])
 def test_workloads_match_oracle(cfg, seqs, layout):
+    # every sequence of every workload, element by element (the oracle result
+    # of a workload is computed once and reused for the three layouts)
     say(f"attention workload {cfg} layout {layout}")
     x = inputs(cfg)
     out, lse = run_gpu(x, flags=layout)
-    if cfg == "ragged":
-        lens = (x["prefix_offsets"][1:] - x["prefix_offsets"][:-1]).tolist()
-        seqs = sorted({0, 1, 9, int(np.argmin(lens)), int(np.argmax(lens)), 33, 63})
     key = (cfg, None if seqs is None else tuple(seqs))
     if key not in _WORKLOAD_REFS:
         _WORKLOAD_REFS[key] = run_oracle(x if seqs is None else subset_sequences(x, seqs))

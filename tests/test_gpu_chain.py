@@ -12,8 +12,10 @@ from gpu_util import ORACLE_THREADS, bf16_round, f64, inputs, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg,paired", [("tiny", False), ("b4", False), ("b8", False), ("b8", True)],
-                         ids=["tiny", "b4", "b8", "b8_paired_head_major"])
+@pytest.mark.parametrize("cfg,paired", [("tiny", False), ("b4", False), ("b8", False), ("b8", True),
+                                        ("b16", False), ("b16", True), ("ragged", True)],
+                         ids=["tiny", "b4", "b8", "b8_paired_head_major", "b16", "b16_paired_head_major",
+                              "ragged_paired_head_major"])
 def test_chain_matches_oracle(cfg, paired):
     say(f"chain {cfg} paired head-major {paired}")
     x = inputs(cfg)

@@ -103,7 +103,7 @@ def test_fused_equals_two_calls_bit_exact(case):
     assert torch.equal(lse[:, rows], ref_lse[:, rows]), "lse differs"
 
 
-@pytest.mark.parametrize("cfg,seqs", [("b8", None), ("b16", [0, 7]), ("ragged", [0, 9, 33])])
+@pytest.mark.parametrize("cfg,seqs", [("b8", None), ("b16", None), ("ragged", None)])
 def test_fused_workloads_match_oracle_chain(cfg, seqs):
     say(f"fused workload {cfg}")
     x = inputs(cfg)
