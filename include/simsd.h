@@ -345,9 +345,11 @@ size_t simsd_accept_workspace(int b, int B, int V);
  *   other arguments as for simsd_accept
  *   workspace, ws_bytes  at least simsd_accept_logits_workspace() bytes,
  *                 256-byte aligned, ALL ZERO before the first call that uses
- *                 it (every call leaves its counters and ready words zero;
- *                 the row statistics area is overwritten). Calls sharing a
- *                 workspace must not run concurrently.
+ *                 it. Every call leaves all of it zero again (counters, ready
+ *                 words and the row statistics, which the acceptance pass
+ *                 clears once the last reader of a sequence is done), so one
+ *                 buffer serves later calls at any sizes it is large enough
+ *                 for. Calls sharing a workspace must not run concurrently.
  * Decisions agree with simsd_accept on the fp32-rounded softmax except where
  * a uniform lies within a few fp32 ulps of its step's ratio, or u_{B+1} * Z
  * within rounding of a CDF step (the exponentials are evaluated in another

@@ -101,6 +101,17 @@ __device__ __forceinline__ RowStats row_stats_of(const AcceptArgs& a, int s, int
   return RowStats{a.row_stats[2 * rt], a.row_stats[2 * rt + 1], a.row_stats[2 * rd], a.row_stats[2 * rd + 1]};
 }
 
+// Zero the statistics of sequence s's 2 B rows (4 B doubles, one per thread)
+// once every workgroup of the sequence has read them, so a call leaves the
+// whole workspace zero and a workspace can be reused at any other sizes.
+__device__ __forceinline__ void clear_row_stats(const AcceptArgs& a, int s, int tid) {
+  const int n = 2 * a.B;  // doubles of one half (target or draft rows)
+  if (tid < 2 * n) {
+    const size_t half = tid < n ? 0 : static_cast<size_t>(a.b) * a.B * 2;
+    a.row_stats[half + static_cast<size_t>(s) * a.B * 2 + tid % n] = 0.0;
+  }
+}
+
 // Masses of entries y0 .. y0+PER-1 of one row: the residual max(0, p - q) in
 // fp32, or p itself for the zero-residual fallback; entries at or past V are 0.
 // LOGITS: prow / qrow are logits rows and p, q their softmax (row stats rs).
@@ -244,6 +255,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   __shared__ int sh_L, sh_stat, sh_last, sh_pick, sh_seg;
   __shared__ double sh_mass[kMaxSegments];
   __shared__ double sh_T, sh_base;
+  __shared__ double sh_rs[4];  // LOGITS: row statistics of the rejected step's rows
 
   const int seg = blockIdx.x, nseg = gridDim.x;
   const int s = blockIdx.y;
@@ -273,6 +285,10 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     } else {
       const int kk = lane < B ? inv_s[lane] : 0;  // position with label lane + 1
       const int x = __shfl(x_k, kk, kWave);
+      // LOGITS: this step's row statistics (the only reads of them in the call)
+      RowStats rs{};
+      if constexpr (LOGITS)
+        if (lane < B) rs = row_stats_of(a, s, kk);
       bool acc = true;
       int stat = 0;
       if (lane < B) {
@@ -284,7 +300,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
           const size_t at = (static_cast<size_t>(s) * B + kk) * V + x;
           float pa, qa;
           if constexpr (LOGITS) {
-            const RowStats rs = row_stats_of(a, s, kk);
             pa = softmax_prob(a.zt[at], rs.mt, rs.st, a.inv_t);
             qa = softmax_prob(a.zd[at], rs.md, rs.sd, a.inv_t);
           } else {
@@ -311,6 +326,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
         sh_L = L;
         sh_stat = st;
       }
+      if constexpr (LOGITS) {
+        if (L < B && lane == L) {  // the rejected step's statistics, for the residual pass
+          sh_rs[0] = rs.mt, sh_rs[1] = rs.st, sh_rs[2] = rs.md, sh_rs[3] = rs.sd;
+        }
+      }
     }
   }
   __syncthreads();
@@ -321,6 +341,19 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
       a.correction[s] = -1;
       if (a.status && sh_stat) atomicOr(&a.status[s], sh_stat);
     }
+    if constexpr (LOGITS) {
+      // the sequence's last workgroup past its reads of the row statistics
+      // clears them (every workgroup of s takes this branch: L is the same)
+      if (tid == 0) {
+        const int prev = __hip_atomic_fetch_add(seq_counter(a, s), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_last = prev == nseg - 1;
+      }
+      __syncthreads();
+      if (sh_last) {
+        clear_row_stats(a, s, tid);
+        if (tid == 0) __hip_atomic_store(seq_counter(a, s), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     return;
   }
 
@@ -329,7 +362,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   const float* qrow = (LOGITS ? a.zd : a.q) + (static_cast<size_t>(s) * B + kstar) * V;
   const bool vec = (V % 4) == 0;
   RowStats rs{};
-  if constexpr (LOGITS) rs = row_stats_of(a, s, kstar);
+  if constexpr (LOGITS) rs = RowStats{sh_rs[0], sh_rs[1], sh_rs[2], sh_rs[3]};
 
   // ---- every workgroup: residual mass of its segment, published with the
   // ready bit; the arrival counter moves without waiting for the publish ----
@@ -346,6 +379,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   }
   __syncthreads();
   if (!sh_last) return;
+  // every workgroup of s has read its row statistics (before its arrival)
+  if constexpr (LOGITS) clear_row_stats(a, s, tid);
 
   // ---- last workgroup: collect the masses, clear the words, locate ----
   bool timed_out = false;

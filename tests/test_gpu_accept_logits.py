@@ -60,15 +60,25 @@ def test_random_logits_and_temperatures(V, b, T):
 
 def test_workspace_left_zero_and_reused():
     V, b, B = 10000, 8, 8
-    rows = 2 * b * B
-    nseg1 = (V + 4095) // 4096
     need = binding.simsd_accept_logits_workspace(b, B, V)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for seed in (1, 2, 3):
         check(*random_logits(V, b, B, seed=seed), 1.0, f"reuse {seed}", ws=ws)
-    # everything but the row statistics (the last rows * 16 bytes) is zero again
-    stats_bytes = (rows * 16 + 255) // 256 * 256
-    assert int(torch.count_nonzero(ws[: need - stats_bytes])) == 0
+        # counters, ready words and row statistics are all zero again
+        assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_workspace_reused_across_sizes():
+    # one buffer sized for the largest call, then calls at other sizes: what a
+    # call leaves behind must never land in another layout's counters or
+    # ready words (statistics of 2 b B rows sit at a size-dependent offset)
+    sizes = [(151936, 8, 8), (20480, 16, 8), (151936, 4, 16), (4097, 32, 4), (151936, 8, 8), (64, 2, 3)]
+    need = max(binding.simsd_accept_logits_workspace(b, B, V) for V, b, B in sizes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (V, b, B) in enumerate(sizes):
+        say(f"shared workspace, call {i}: V={V} b={b} B={B}")
+        check(*random_logits(V, b, B, seed=100 + i, spread=3.0), 1.0, f"shared ws V={V} b={b}", ws=ws)
+        assert int(torch.count_nonzero(ws)) == 0
 
 
 def test_edge_cases():
@@ -93,3 +103,14 @@ def test_edge_cases():
     one = np.zeros((3, 2, 1), np.float32)
     check(one, one, np.zeros((3, 2), np.int32), np.tile(np.array([[2, 1]], np.int32), (3, 1)),
           rng.random((3, 3)).astype(np.float32), 1.0, "V=1")
+
+
+@pytest.mark.parametrize("V,b,per", [(151936, 8, 16), (151936, 8, 64), (20480, 16, 64), (12289, 4, 16),
+                                     (4097, 32, 64)])
+def test_row_statistics_segment_widths(V, b, per):
+    # a row's maximum and sum of exp do not depend on how the statistics pass
+    # cuts the row into segments (256 per entries each, folded by the row's
+    # last arrival); V=4097 leaves a one-entry last segment
+    say(f"accept from logits V={V} b={b}, row-statistics segments of {256 * per}")
+    with binding.tuning(rowstat_per=per):
+        check(*random_logits(V, b, seed=per + V, spread=3.0), 1.0, f"V={V} per={per}")
