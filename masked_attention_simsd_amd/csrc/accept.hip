@@ -84,6 +84,36 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   return under ? 0.0 : ldexp(e, static_cast<int>(n));
 }
 
+// exp(x) for x <= 0 in fp64 by table (Tang's method), for the statistics
+// pass where it runs once per logit and its instruction count sets the pass's
+// speed: x = (64 n + j) ln2/64 + r with |r| <= ln2/128 (k = 64 n + j from a
+// round-to-nearest shifter, ln2/64 in two parts), e^x = 2^n T[j] (1 + p(r))
+// with T[j] = 2^(j/64) from `tab` and p the Taylor series of e^r - 1 to
+// degree 5 (truncation < 4e-17); 2^n is added to the exponent field.
+// Relative error a few 1e-16. x is first clamped to [-708, 0] (NaN as well):
+// below that the true value is under 3.4e-308 and the result, 3.3e-308, is
+// equally invisible in a row sum of at least 1 (it keeps n >= -1022 with
+// T[j](1 + p) >= 1, so the scaled result stays normal).
+__device__ __forceinline__ double exp_nonpos_tab(double x, const double* tab) {
+  x = fmax(x, -708.0);
+  constexpr double kShift = 6755399441055744.0;  // 1.5 * 2^52: k lands in the low word
+  const double kt = __builtin_fma(x, 92.332482616893658, kShift);  // x * 64 / ln2 + shift
+  const int k = __double2loint(kt);
+  const double kd = kt - kShift;
+  double r = __builtin_fma(-kd, 0x1.62e42fefa39efp-7, x);  // ln2/64, high part
+  r = __builtin_fma(-kd, 0x1.abc9e3b39803fp-62, r);        // ln2/64, low part
+  double p = 1.0 / 120.0;
+  p = __builtin_fma(p, r, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p *= r;
+  const double t = tab[k & 63];
+  const double e = __builtin_fma(t, p, t);
+  const int hi = __double2hiint(e) + ((k >> 6) << 20);  // arithmetic shift: floor(k / 64)
+  return __hiloint2double(hi, __double2loint(e));
+}
+
 // Softmax probability of logit z in a row with statistics (max m, sum of
 // exp s, passed as 1/s) at inverse temperature inv_t: exp((z - m) inv_t) / s
 // in fp64, rounded once to fp32 (the precision the decisions are taken in).
@@ -498,34 +528,44 @@ __device__ float block_max_all(float v) {
 // maximum -- and publishes both with ready bits; the row's last arrival
 // collects them, folds S = sum_j s_j exp((m_j - M) / T) with M = max_j m_j in a
 // fixed order, writes (M, S) and clears its words and counter.
-template <int PER1>
+template <int PER1, bool UNIT_T>
 __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
   constexpr int SEG1 = PER1 * kAccThreads;
   __shared__ int sh_last;
+  __shared__ double tab[64];  // 2^(j/64)
   const int nrow_half = a.b * a.B;
   const long id = blockIdx.x;
   const int row = static_cast<int>(id / a.nseg1), seg = static_cast<int>(id % a.nseg1);
   const int V = a.V, tid = threadIdx.x;
   const float* z = (row < nrow_half ? a.zt : a.zd) + static_cast<size_t>(row % nrow_half) * V;
-  const int y0 = seg * SEG1 + PER1 * tid;
+  // thread tid takes the 4-entry pieces seg SEG1 + 4 (tid + 256 j): each load
+  // instruction of a wave reads 1 KB of contiguous logits
+  const int y0 = seg * SEG1 + 4 * tid;
   float v[PER1];
-  if ((V % 4) == 0 && y0 + PER1 <= V) {
 #pragma unroll
-    for (int j = 0; j < PER1 / 4; ++j) {
-      const float4 f = *reinterpret_cast<const float4*>(z + y0 + 4 * j);
+  for (int j = 0; j < PER1 / 4; ++j) {
+    const int y = y0 + j * 4 * kAccThreads;
+    if ((V % 4) == 0) {
+      float4 f = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (y < V) f = *reinterpret_cast<const float4*>(z + y);
       v[4 * j] = f.x, v[4 * j + 1] = f.y, v[4 * j + 2] = f.z, v[4 * j + 3] = f.w;
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int e = 0; e < PER1; ++e) v[e] = y0 + e < V ? z[y0 + e] : -INFINITY;
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = y + e < V ? z[y + e] : -INFINITY;
+    }
   }
+  if (tid < 64) tab[tid] = exp2(tid * (1.0 / 64.0));  // visible after the barrier in block_max_all
   float tm = -INFINITY;
 #pragma unroll
   for (int e = 0; e < PER1; ++e) tm = fmaxf(tm, v[e]);
   const float m = block_max_all(tm);
   double ts = 0.0;
+  const double md = static_cast<double>(m), inv_t = a.inv_t;
 #pragma unroll
-  for (int e = 0; e < PER1; ++e) ts += exp_nonpos((static_cast<double>(v[e]) - static_cast<double>(m)) * a.inv_t);
+  for (int e = 0; e < PER1; ++e) {
+    const double x = static_cast<double>(v[e]) - md;  // exact
+    ts += exp_nonpos_tab(UNIT_T ? x : x * inv_t, tab);
+  }
   const double sum = block_sum(ts);
 
   unsigned long long* words = a.row_words + static_cast<size_t>(row) * a.nseg1 * 2;
@@ -634,11 +674,18 @@ hipError_t launch_accept_mode(const AcceptArgs& a, hipStream_t stream) {
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) { return launch_accept_mode<false>(a, stream); }
 
-// Entries per thread of the row-statistics pass: the tuning override
+// Entries per thread of the row-statistics pass: 16 (4096-entry segments).
+// The pass is bound by VALU issue (about 19 instructions per logit with the
+// table exp, every one a 4-cycle wave issue) more than by HBM, so the shortest
+// segments, whose workgroups (56 VGPRs, 8 waves per SIMD) overlap one
+// another's loads and arithmetic best, win (one MI355X, kernel trace, 16 / 32
+// / 64 per thread: V = 151936 with 256 rows -> 43.6 / 45.1 / 46.4 us; V =
+// 32768 with 1024 rows -> 37.6 / 41.0 / 42.2 us; a variant streaming longer
+// runs with prefetch measured 42.9 us on the first). The tuning override
 // SIMSD_TUNE_ROWSTAT_PER = 16, 32 or 64 replaces the default.
 int row_stat_per() {
   const int forced = tuning(SIMSD_TUNE_ROWSTAT_PER);
-  return (forced == 16 || forced == 32 || forced == 64) ? forced : 32;
+  return (forced == 16 || forced == 32 || forced == 64) ? forced : 16;
 }
 
 hipError_t launch_accept_logits(const AcceptArgs& a0, hipStream_t stream) {
@@ -647,12 +694,15 @@ hipError_t launch_accept_logits(const AcceptArgs& a0, hipStream_t stream) {
   a.nseg1 = (a.V + kAccThreads * per1 - 1) / (kAccThreads * per1);
   const long units = 2L * a.b * a.B * a.nseg1;
   const dim3 grid(static_cast<unsigned>(units)), block(kAccThreads);
+  // T = 1 (inverse temperature exactly 1) skips a multiply per logit
+  const bool unit = a.inv_t == 1.0;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
   if (per1 == 16)
-    hipLaunchKernelGGL(row_stats_kernel<16>, grid, block, 0, stream, a);
+    unit ? go(row_stats_kernel<16, true>) : go(row_stats_kernel<16, false>);
   else if (per1 == 32)
-    hipLaunchKernelGGL(row_stats_kernel<32>, grid, block, 0, stream, a);
+    unit ? go(row_stats_kernel<32, true>) : go(row_stats_kernel<32, false>);
   else
-    hipLaunchKernelGGL(row_stats_kernel<64>, grid, block, 0, stream, a);
+    unit ? go(row_stats_kernel<64, true>) : go(row_stats_kernel<64, false>);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_accept_mode<true>(a, stream);
