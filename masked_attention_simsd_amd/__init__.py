@@ -2,17 +2,20 @@
 
 The compute path is libsimsd.so (HIP kernels behind the C ABI of
 include/simsd.h); ``binding`` exposes its entry points to Python under the
-same names. ``synth`` draws the seeded synthetic inputs.
+same names (every name in ``binding.EXPORTS``, plus the binding's flags,
+status codes and helpers), and they are re-exported here on first use.
+``synth`` draws the seeded synthetic inputs.
 """
+import importlib
 
-_BINDING_NAMES = (
-    "simsd_rope_copy", "simsd_verify_attention", "simsd_verify_attention_workspace",
-    "simsd_accept", "SimsdError", "load_library",
-)
+_SUBMODULES = ("binding", "synth", "build")
 
 
 def __getattr__(name):
-    if name in _BINDING_NAMES:
-        from . import binding
+    # lazy: importing the package does not load torch or the library
+    if name.startswith("_") or name in _SUBMODULES:
+        raise AttributeError(name)
+    binding = importlib.import_module(__name__ + ".binding")
+    if hasattr(binding, name):
         return getattr(binding, name)
     raise AttributeError(name)

@@ -50,3 +50,14 @@ def test_missing_library_is_an_error(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         binding.load_library(str(tmp_path / "libsimsd.so"))
+
+
+def test_package_reexports_every_entry_point():
+    import masked_attention_simsd_amd as pkg
+    from masked_attention_simsd_amd import binding
+    # every C entry point the binding wraps under its own name (the status
+    # string and last-error calls are used inside the binding only)
+    wrapped = [n for n in binding.EXPORTS if hasattr(binding, n)]
+    assert len(wrapped) >= len(binding.EXPORTS) - 2
+    for name in wrapped + ["SimsdError", "load_library", "tuning", "SIMSD_ROPE_POSITIONS"]:
+        assert getattr(pkg, name) is getattr(binding, name), name
