@@ -8,17 +8,21 @@ HBM. The form with RoPE-copy fused into the attention launch
 timed beside it. At least ceil(1 GB / prefix KV bytes) input sets are rotated so the
 prefix KV of a step is not served from the 256 MB MALL.
 
-Order of work: one step on fresh inputs (kept for the parity check); each
-entry point alone (10 untimed launches, then launches timed back to back and
-one by one); the headline steps (--warmup untimed, then exactly --steps
-between one event pair); the fused steps; single-step spread; finally the CPU
-oracle on the host cores, whose first result checks the kept step.
+Order of work: one step on fresh inputs (kept for the parity check); about
+20 ms of untimed steps (the clocks come up); each entry point alone, 10
+untimed launches then launches timed one by one; the
+headline steps (--warmup untimed, then exactly --steps between one event
+pair); the fused steps, then both step forms in alternating rounds;
+single-step spread; each entry point back to back (last of the GPU regions:
+a long unbroken run of launches slows the chip for a while after it);
+finally the CPU oracle on the host cores, whose first result checks the kept
+step.
 
 Prints one JSON line: verified blocks/s (one block = one sequence's paired
 2B block through one attention layer plus acceptance), the attention kernel's
-HBM roofline figures (its mean duration over single launches, each between
-its own HIP event pair on the launch stream), each kernel's back-to-back and
-single-launch times, the spread of per-step times, the parity of the kept
+HBM roofline figures (its mean duration inside 200 whole steps, each of its
+launches between its own HIP event pair on the launch stream), each kernel's
+back-to-back and single-launch (alone) times, the spread of per-step times, the parity of the kept
 step against the oracle (attention max-abs, equal accepted lengths, token
 mismatches and the counted near-CDF-boundary cases) and the oracle's
 throughput on the host cores (all cores, and one core).
@@ -33,6 +37,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -181,7 +186,6 @@ def summarize_rocprof(path: str):
     import csv
     import glob
     import sqlite3
-    import statistics
 
     for f in sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True)):
         print(f"# kernel dispatches: {os.path.relpath(f, path)}")
@@ -343,40 +347,36 @@ def main():
 
     n_k = max(args.steps, 200)  # launches per kernel region
 
-    def alone(fn, idx):
+    def singles(fn, calls_, idx):
         """One entry point alone on the stream, over the rotated input sets:
-        10 untimed launches, then n_k back to back between one event pair
-        (mean time per launch, inter-launch gaps included), then n_k each
-        between its own event pair (median / p10 / p90 of single launches)."""
+        10 untimed launches, then n_k launches each between its own event pair
+        (median / p10 / p90 / mean of single launches)."""
         for i in range(10):
-            if fn(*calls[i % len(calls)][idx]):
+            if fn(*calls_[i % len(calls_)][idx]):
                 raise RuntimeError("libsimsd call failed")
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for i in range(n_k):
-            if fn(*calls[i % len(calls)][idx]):
-                raise RuntimeError("libsimsd call failed")
-        e1.record(stream)
         pairs = [(ev(), ev()) for _ in range(n_k)]
         for i, (a0, a1) in enumerate(pairs):
             a0.record(stream)
-            fn(*calls[i % len(calls)][idx])
+            fn(*calls_[i % len(calls_)][idx])
             a1.record(stream)
         torch.cuda.synchronize()
         single = sorted(a0.elapsed_time(a1) * 1e3 for a0, a1 in pairs)
         q = lambda f: single[min(len(single) - 1, int(f * len(single)))]
-        return {"back_to_back_us": round(e0.elapsed_time(e1) / n_k * 1e3, 3),
-                "single_p10_p50_p90_us": [round(q(0.1), 3), round(q(0.5), 3), round(q(0.9), 3)],
+        return {"single_p10_p50_p90_us": [round(q(0.1), 3), round(q(0.5), 3), round(q(0.9), 3)],
                 "single_mean_us": round(sum(single) / len(single), 3)}
 
-    # each entry point alone (the attention kernel first: it is the roofline
-    # kernel); these regions also bring the GPU to its working clocks before
-    # the headline steps
-    k_attn = alone(lib.simsd_verify_attention, 1)
-    k_rope = alone(lib.simsd_rope_copy, 0)
-    k_acc = alone(lib.simsd_accept, 2)
-    k_fused = alone(lib.simsd_verify_attention_rope, 3)
-    k_logits = alone(lib.simsd_accept_logits, 4)
+    def burst(fn, calls_, idx):
+        """n_k launches of one entry point back to back between one event pair
+        (mean time per launch, inter-launch gaps included)."""
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for i in range(n_k):
+            if fn(*calls_[i % len(calls_)][idx]):
+                raise RuntimeError("libsimsd call failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / n_k * 1e3, 3)
+
     # KV commit of set 0's accepted drafts, appended call after call to a
     # paired head-major cache whose regions have room for every call (one
     # launch per call: each sequence's workgroup copies its rows and advances
@@ -393,13 +393,28 @@ def main():
                    P(ext[b + 1:]), P(cpos), P(cpos), b, B, Hkv, d, KV_LAYOUT, None, hs)
     rows = int(par_L.sum().item())
     calls_commit = [(commit_call,)]
-    saved = calls
-    calls = calls_commit
-    k_commit = alone(lib.simsd_commit_kv, 0)
-    calls = saved
+    entries = {"verify_attention": (lib.simsd_verify_attention, calls, 1),
+               "rope_copy": (lib.simsd_rope_copy, calls, 0),
+               "accept": (lib.simsd_accept, calls, 2),
+               "verify_attention_rope": (lib.simsd_verify_attention_rope, calls, 3),
+               "accept_logits": (lib.simsd_accept_logits, calls, 4),
+               "commit_kv": (lib.simsd_commit_kv, calls_commit, 0)}
+    # Untimed steps for about 20 ms first: from idle the chip runs slow until
+    # its clocks come up (single attention launches measured 60-72 us on b8
+    # when timed first). Then single launches of each entry point (the
+    # attention kernel first: it is the roofline kernel), before any long
+    # back-to-back run, which slows the chip for a while after it (single
+    # launches right after 200 back-to-back attention launches measured about
+    # 58 us on b8, settling to 53-55 us).
+    t_w = time.perf_counter()
+    n_w = 0
+    while time.perf_counter() - t_w < 0.02 or n_w < 50:
+        step(n_w)
+        n_w += 1
+        if n_w % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    if int(ext[b + 1:].sum().item()) != rows * n_commit:
-        raise RuntimeError("commit timing: lengths did not advance as expected")
+    kern = {name: singles(*e) for name, e in entries.items()}
 
     # the headline: W untimed steps, then exactly K steps between one event pair
     for i in range(args.warmup):
@@ -424,15 +439,53 @@ def main():
     f1.record(stream)
     torch.cuda.synchronize()
     fused_step_ms = f0.elapsed_time(f1) / args.steps
-    # spread of single steps: an event pair around each step
-    pairs = [(ev(), ev()) for _ in range(n_k)]
-    for i, (e0, e1) in enumerate(pairs):
+    # The same comparison in alternating rounds (three-launch, fused, ...), so
+    # that neither form is timed in a different clock state: a run of
+    # back-to-back launches slows as it goes on, and the region above always
+    # follows the headline steps.
+    ab_rounds, ab = 4, {"three_launch": [], "fused": []}
+    for r in range(ab_rounds):
+        for name, fn in (("three_launch", step), ("fused", step_fused)) if r % 2 == 0 else \
+                (("fused", step_fused), ("three_launch", step)):
+            a0, a1 = ev(), ev()
+            a0.record(stream)
+            for i in range(args.steps):
+                fn(i)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            ab[name].append(a0.elapsed_time(a1) / args.steps * 1e3)
+    step_ab = {k: round(statistics.median(v), 3) for k, v in ab.items()}
+    # spread of single steps: an event pair around each step, and one around
+    # the attention launch inside it -- the roofline kernel's duration under
+    # the conditions of the steps themselves (the clocks the chip holds depend
+    # on its recent load: slower from idle and during long unbroken runs)
+    pairs = [(ev(), ev(), ev(), ev()) for _ in range(n_k)]
+    for i, (e0, a0, a1, e1) in enumerate(pairs):
+        rope, attn, acc = calls[i % len(calls)][:3]
         e0.record(stream)
-        step(i)
+        rc = lib.simsd_rope_copy(*rope)
+        a0.record(stream)
+        rc |= lib.simsd_verify_attention(*attn)
+        a1.record(stream)
+        rc |= lib.simsd_accept(*acc)
         e1.record(stream)
+        if rc:
+            raise RuntimeError(f"libsimsd returned {rc}")
     torch.cuda.synchronize()
-    per_step = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+    per_step = sorted(e0.elapsed_time(e1) * 1e3 for e0, _, _, e1 in pairs)
     pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
+    in_step = sorted(a0.elapsed_time(a1) * 1e3 for _, a0, a1, _ in pairs)
+    qs = lambda f: in_step[min(len(in_step) - 1, int(f * len(in_step)))]
+    attn_in_steps = {"p10_p50_p90_us": [round(qs(0.1), 3), round(qs(0.5), 3), round(qs(0.9), 3)],
+                     "mean_us": round(sum(in_step) / len(in_step), 3)}
+    # last, each entry point back to back (after every other GPU region)
+    for name, e in entries.items():
+        kern[name] = dict({"back_to_back_us": burst(*e)}, **kern[name])
+    torch.cuda.synchronize()
+    if int(ext[b + 1:].sum().item()) != rows * n_commit:
+        raise RuntimeError("commit timing: lengths did not advance as expected")
+    k_attn, k_rope, k_acc = kern["verify_attention"], kern["rope_copy"], kern["accept"]
+    k_fused, k_logits, k_commit = kern["verify_attention_rope"], kern["accept_logits"], kern["commit_kv"]
 
     # CPU baseline (the oracle on the host cores) and the parity of the first
     # step against it
@@ -465,7 +518,7 @@ def main():
                "single_core": {"value": round(cpu1_bps, 3), "unit": "blocks/s",
                                "sample": f"{reps1} passes over the first {n1} sequences in {secs1:.1f} s"}}
 
-    attn_avg_s = k_attn["single_mean_us"] / 1e6
+    attn_avg_s = attn_in_steps["mean_us"] / 1e6
     nbytes, flops = attn_bytes_flops(w, lens, fused=False)
     achieved = nbytes / attn_avg_s / 1e9
     tflops = flops / attn_avg_s / 1e12
@@ -497,10 +550,12 @@ def main():
                      "avg_launch_us": round(attn_avg_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": nbytes},
         "kernels_us": {"launches_per_kernel": n_k,
-                       "verify_attention": k_attn, "rope_copy": k_rope, "accept": k_acc,
+                       "verify_attention": dict(k_attn, in_steps=attn_in_steps),
+                       "rope_copy": k_rope, "accept": k_acc,
                        "step_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                        "fused_rope": {"verify_attention_rope": k_fused,
-                                      "step": round(fused_step_ms * 1e3, 3)},
+                                      "step": round(fused_step_ms * 1e3, 3),
+                                      "steps_alternating_us": dict(step_ab, rounds=ab_rounds)},
                        "accept_logits": dict(k_logits, logits_GBps=round(
                            2 * b * B * w.V * 4 / k_logits["single_p10_p50_p90_us"][1] / 1e3, 1)),
                        "commit_kv": dict(k_commit, rows_committed=rows,
