@@ -449,7 +449,8 @@ int simsd_commit_kv(const void* k_blk, const void* v_blk, const int32_t* tau, co
  *   SIMSD_TUNE_ATTN_XCD_REMAP  0/1: keep a unit's splits on one XCD
  *   SIMSD_TUNE_ATTN_ROTATE     0/1: per-unit starting prefix tile
  *   SIMSD_TUNE_ATTN_LPT        0/1: longest-first order of unsplit launches
- *   SIMSD_TUNE_ATTN_SHIFT      prefix keys moved off split 0 (>= 0)
+ *   SIMSD_TUNE_ATTN_SHIFT      prefix keys moved off split 0 (>= 0; default: one key
+ *                              tile per block tile of the variant launched)
  *   SIMSD_TUNE_ACCEPT_PER      acceptance entries per thread: 4, 8 or 16
  *   SIMSD_TUNE_ROWSTAT_PER     row-statistics entries per thread: 16, 32 or 64
  * Returns SIMSD_OK, or SIMSD_ERR_SIZE for an unknown key or a value below -1.

@@ -92,7 +92,7 @@ struct AttnArgs {
   int M;              // query rows per (sequence, KV head) = nrows * G
   int row_slices;     // ceil(M / rows per workgroup)
   int chunk;          // prefix keys per split (multiple of the key tile)
-  int shift;          // split 0 runs chunk - shift keys, split k >= 1 starts at k * chunk - shift
+  int shift;          // split 0 runs chunk - shift keys, split k >= 1 starts at k * chunk - shift (-1: the launch picks)
   int nsplit;         // splits per (sequence, KV head, row slice)
   int max_prefix;
   int total_real;     // b * Hkv * row_slices * nsplit

@@ -1099,7 +1099,17 @@ inline size_t rope_table_bytes(const AttnArgs& a) {
 }
 
 template <int D, int NWC, int QB, int TK, int NS, int NW = 4, int KS = 1, int MODE = kModeTau>
-hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_variant(const AttnArgs& a0, hipStream_t stream) {
+  AttnArgs a = a0;
+  if (a.shift < 0) {
+    // Split 0 also streams the block tiles, so by default it gives up one
+    // tile's worth of prefix keys per block tile of this variant (capped at
+    // half a chunk), which evens out the splits' finish times (one MI355X,
+    // interleaved runs: b8 54.9 -> 54.3 us, b16 108.4 -> 107.2 us, b = 1
+    // prefix 1024 17.0 -> 16.2 us; larger shifts measured slower on b8).
+    const int blk_tiles = (a.nblk + TK - 1) / TK;
+    a.shift = a.nsplit > 1 ? std::min(a.chunk / 2, blk_tiles * TK) : 0;
+  }
   dim3 grid(static_cast<unsigned>(a.total_grid)), block(NW * 64);
   const size_t dyn = MODE == kModeTauRope ? rope_table_bytes(a) : 0;
   if (a.out_f32)
@@ -1276,9 +1286,11 @@ AttnPlan plan_attention_rows(int b, int nrows, int Hq, int Hkv, int d, int max_p
   p.nsplit = nsplit;
   // tuning: SIMSD_TUNE_ATTN_LPT = 0 / 1 forces the longest-first order off / on
   p.lpt = (tuned(SIMSD_TUNE_ATTN_LPT, lpt_ring ? 1 : 0) != 0 && lpt_ok) ? 1 : 0;
-  // tuning: prefix keys moved off split 0, which also takes the block tiles
-  // (SIMSD_TUNE_ATTN_SHIFT; measured neutral on MI355X, so 0 by default)
-  p.shift = std::max(0, std::min(chunk / 2, tuned(SIMSD_TUNE_ATTN_SHIFT, 0)));
+  // prefix keys moved off split 0, which also takes the block tiles: -1
+  // (default) lets the launch take one tile's worth per block tile of the
+  // variant it runs; SIMSD_TUNE_ATTN_SHIFT >= 0 fixes it
+  const int shift_set = tuned(SIMSD_TUNE_ATTN_SHIFT, -1);
+  p.shift = shift_set < 0 ? -1 : std::min(chunk / 2, shift_set);
   const size_t us = static_cast<size_t>(units);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   // The counter words sit in a region of fixed size at the start of every
