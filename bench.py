@@ -455,6 +455,50 @@ def main():
             torch.cuda.synchronize()
             ab[name].append(a0.elapsed_time(a1) / args.steps * 1e3)
     step_ab = {k: round(statistics.median(v), 3) for k, v in ab.items()}
+    # Two independent batches in flight: even steps on this stream, odd steps
+    # on a second one (default priority) with its own workspaces and its own
+    # input sets, so one batch's short latency-bound kernels (RoPE-copy,
+    # acceptance) can run beside the other's attention. Reported beside the
+    # headline, which keeps one batch at a time.
+    two = None
+    n_pairs = len(calls) // 2
+    if n_pairs >= 1:
+        s2 = torch.cuda.Stream()
+        hs2 = ctypes.c_void_p(s2.cuda_stream)
+        ws2 = torch.zeros_like(ws)
+        ws_acc2 = torch.zeros_like(ws_acc)
+
+        def on_stream2(c):
+            rope, attn, acc = c[:3]
+            attn = attn[:18] + (P(ws2), ws2.numel(), hs2)
+            acc = acc[:11] + (P(ws_acc2), ws_acc2.numel(), hs2)
+            return rope[:10] + (hs2,), attn, acc
+
+        lanes = [[calls[2 * j][:3] for j in range(n_pairs)], [on_stream2(calls[2 * j + 1]) for j in range(n_pairs)]]
+
+        def step2(i):
+            rope, attn, acc = lanes[i % 2][(i // 2) % n_pairs]
+            rc = lib.simsd_rope_copy(*rope)
+            rc |= lib.simsd_verify_attention(*attn)
+            rc |= lib.simsd_accept(*acc)
+            if rc:
+                raise RuntimeError(f"libsimsd returned {rc}")
+
+        for i in range(2 * args.warmup):
+            step2(i)
+        torch.cuda.synchronize()
+        d0, d1, d2 = ev(), ev(), ev()
+        d0.record(stream)
+        s2.wait_event(d0)
+        for i in range(args.steps):
+            step2(i)
+        d2.record(s2)
+        stream.wait_event(d2)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        two_ms = d0.elapsed_time(d1)
+        two = {"streams": 2, "steps": args.steps, "ms_per_step": round(two_ms / args.steps, 5),
+               "blocks_per_s": round(b * args.steps / (two_ms / 1e3), 1)}
     # spread of single steps: an event pair around each step, and one around
     # the attention launch inside it -- the roofline kernel's duration under
     # the conditions of the steps themselves (the clocks the chip holds depend
@@ -556,6 +600,7 @@ def main():
                        "fused_rope": {"verify_attention_rope": k_fused,
                                       "step": round(fused_step_ms * 1e3, 3),
                                       "steps_alternating_us": dict(step_ab, rounds=ab_rounds)},
+                       "two_batches_in_flight": two,
                        "accept_logits": dict(k_logits, logits_GBps=round(
                            2 * b * B * w.V * 4 / k_logits["single_p10_p50_p90_us"][1] / 1e3, 1)),
                        "commit_kv": dict(k_commit, rows_committed=rows,
