@@ -68,6 +68,18 @@ def test_workspace_left_zero_and_reused():
         assert int(torch.count_nonzero(ws)) == 0
 
 
+@pytest.mark.parametrize("V,b,B", [(4097, 4, 64), (32768, 3, 64), (1000, 64, 1)])
+def test_block_sizes_and_workspace_left_zero(V, b, B):
+    # B = 64: all 256 threads of a workgroup clear the sequence's 4 B row
+    # statistics; B = 1: a single step per sequence
+    say(f"accept from logits V={V} b={b} B={B}")
+    need = binding.simsd_accept_logits_workspace(b, B, V)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for seed in (1, 2):
+        check(*random_logits(V, b, B, seed=seed + V + B), 1.0, f"V={V} b={b} B={B}", ws=ws)
+        assert int(torch.count_nonzero(ws)) == 0
+
+
 def test_workspace_reused_across_sizes():
     # one buffer sized for the largest call, then calls at other sizes: what a
     # call leaves behind must never land in another layout's counters or
