@@ -63,3 +63,29 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_committed_bench_lines_follow_the_contract():
+    # every line in profiles/bench_lines.txt carries the contract's keys, and
+    # its roofline figures are the algorithmic bytes over the reported launch
+    # time (no figure typed in by hand)
+    import json
+    lines = [l for l in open(os.path.join(ROOT, "profiles", "bench_lines.txt")) if not l.startswith("#")]
+    assert len(lines) == 3
+    for l in lines:
+        w, j = l.split(": ", 1)
+        d = json.loads(j)
+        for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                    "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "parity"):
+            assert key in d, (w, key)
+        assert d["n_gpus"] == 1 and d["dtype"] == "bf16" and d["metric"] == bench.METRIC
+        r = d["roofline"]
+        x = synth.make_inputs(w, with_accept=False, with_attn=False)
+        nbytes, _ = bench.attn_bytes_flops(synth.CONFIGS[w], x["prefix_lens"].tolist(), fused=False)
+        assert r["algorithmic_bytes_per_launch"] == nbytes
+        assert abs(r["achieved"] - nbytes / r["avg_launch_us"] / 1e3) <= 0.1
+        assert abs(r["frac"] - r["achieved"] / r["peak"]) <= 1e-4
+        assert r["avg_launch_us"] == d["kernels_us"]["verify_attention"]["in_steps"]["mean_us"]
+        assert abs(d["value"] - d["config"]["global_batch"] / d["ms_per_step"] * 1e3) / d["value"] < 2e-3
+        if w == "b8":
+            assert d["cpu_baseline"] is not None and d["parity"]["accept_len_equal"] == 16
