@@ -349,9 +349,12 @@ def main():
 
     def singles(fn, calls_, idx):
         """One entry point alone on the stream, over the rotated input sets:
-        10 untimed launches, then n_k launches each between its own event pair
-        (median / p10 / p90 / mean of single launches)."""
-        for i in range(10):
+        100 untimed launches, then n_k launches each between its own event pair
+        (median / p10 / p90 / mean of single launches). The untimed launches
+        keep the GPU busy while the host queues the timed ones ahead of it, so
+        no event pair also times the host's launch latency (a timestamp taken
+        on an idle GPU would run on until the host had issued the kernel)."""
+        for i in range(100):
             if fn(*calls_[i % len(calls_)][idx]):
                 raise RuntimeError("libsimsd call failed")
         pairs = [(ev(), ev()) for _ in range(n_k)]
@@ -381,7 +384,7 @@ def main():
     # paired head-major cache whose regions have room for every call (one
     # launch per call: each sequence's workgroup copies its rows and advances
     # its length)
-    n_commit = 10 + 2 * n_k
+    n_commit = 100 + 2 * n_k  # untimed + single + back-to-back launches
     cap = (n_commit + 1) * B
     kvc = torch.empty(Hkv, b * cap, 2, d, dtype=torch.bfloat16, device=dev)
     kc, vc = binding.kv_pair_views(kvc)
@@ -504,6 +507,8 @@ def main():
     # the conditions of the steps themselves (the clocks the chip holds depend
     # on its recent load: slower from idle and during long unbroken runs)
     pairs = [(ev(), ev(), ev(), ev()) for _ in range(n_k)]
+    for i in range(100):  # untimed, so the host runs ahead of the GPU (see singles)
+        step(i)
     for i, (e0, a0, a1, e1) in enumerate(pairs):
         rope, attn, acc = calls[i % len(calls)][:3]
         e0.record(stream)
