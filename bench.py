@@ -9,14 +9,14 @@ timed beside it. At least ceil(1 GB / prefix KV bytes) input sets are rotated so
 prefix KV of a step is not served from the 256 MB MALL.
 
 Order of work: one step on fresh inputs (kept for the parity check); about
-20 ms of untimed steps (the clocks come up); each entry point alone, 10
-untimed launches then launches timed one by one; the
-headline steps (--warmup untimed, then exactly --steps between one event
-pair); the fused steps, then both step forms in alternating rounds;
-single-step spread; each entry point back to back (last of the GPU regions:
-a long unbroken run of launches slows the chip for a while after it);
-finally the CPU oracle on the host cores, whose first result checks the kept
-step.
+20 ms of untimed steps (the clocks come up); each entry point alone, 100
+untimed launches then launches timed one by one; the headline steps
+(--warmup untimed, then exactly --steps between one event pair); the fused
+steps, then both step forms in alternating rounds; two batches in flight on
+two streams; 100 untimed steps, then steps with the attention launch timed
+inside each; each entry point back to back (last of the GPU regions: a long
+unbroken run of launches slows the chip for a while after it); finally the
+CPU oracle on the host cores, whose first result checks the kept step.
 
 Prints one JSON line: verified blocks/s (one block = one sequence's paired
 2B block through one attention layer plus acceptance), the attention kernel's
