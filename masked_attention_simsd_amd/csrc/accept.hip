@@ -486,14 +486,20 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
         if (hit < 0 && base + (excl + run) > T) hit = y0 + e;
       }
     }
-    if (hit >= 0) atomicMin(&sh_pick, hit);
+    // Entries grow with the thread index, so the pick is the hit of the
+    // lowest hitting lane of the lowest such wave: one LDS atomic per wave.
+    // (Every thread past the crossing also hits; one atomic per thread queued
+    // up to 256 of them on one LDS word, about 2 us on b8.)
+    const unsigned long long hits = __ballot(hit >= 0);
+    if (hits && lane == __ffsll(static_cast<long long>(hits)) - 1) atomicMin(&sh_pick, hit);
     __syncthreads();
     const bool none = sh_pick == 0x7fffffff;
     __syncthreads();
     if (none) {  // rounding: no crossing inside the segment; take its last positive entry
       if (tid == 0) sh_pick = -1;
       __syncthreads();
-      if (lastpos >= 0) atomicMax(&sh_pick, lastpos);
+      const unsigned long long pos = __ballot(lastpos >= 0);
+      if (pos && lane == 63 - __clzll(static_cast<long long>(pos))) atomicMax(&sh_pick, lastpos);
     }
   } else if (tid == 0) {
     sh_pick = -1;  // no mass at all: nothing can be drawn
