@@ -180,20 +180,61 @@ __device__ __forceinline__ void load_masses(const float* prow, const float* qrow
   }
 }
 
+// Wave-level scans by DPP (row shifts and row broadcasts move data between
+// lanes inside the VALU; the lane shuffles they replace went through LDS, two
+// permutes per fp64 step). An fp64 value moves as its two 32-bit halves;
+// lanes whose source lies outside the row (bound_ctrl) or whose row the row
+// mask leaves out read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
+// Inclusive prefix sum over the 64 lanes in lane order: shifts by 1, 2, 4, 8
+// inside each row of 16, then the last lane of row 0 / 2 into rows 1 / 3
+// (row_bcast:15) and the last lane of row 1 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x += dpp_f64<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_f64<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_f64<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_f64<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_f64<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_f64<0x143, 0xc>(x);  // row_bcast:31
+  return x;
+}
+// The inclusive scan shifted up by one lane (lane 0: 0), i.e. the exclusive scan.
+__device__ __forceinline__ double wave_shift_up1(double incl) { return dpp_f64<0x138, 0xf>(incl); }  // wave_shr:1
+__device__ __forceinline__ double wave_last(double v) {  // lane 63's value, in every lane
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), kWave - 1),
+                          __builtin_amdgcn_readlane(__double2loint(v), kWave - 1));
+}
+
+// Maximum over the 64 lanes, in every lane: the same row shifts and row
+// broadcasts, with lanes that have no source keeping -inf (bound_ctrl off).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_src(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_max_src<0x111, 0xf>(x));
+  x = fmaxf(x, dpp_max_src<0x112, 0xf>(x));
+  x = fmaxf(x, dpp_max_src<0x114, 0xf>(x));
+  x = fmaxf(x, dpp_max_src<0x118, 0xf>(x));
+  x = fmaxf(x, dpp_max_src<0x142, 0xa>(x));
+  x = fmaxf(x, dpp_max_src<0x143, 0xc>(x));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+
 // Exclusive prefix sum (thread order) of one fp64 value per thread, and the
 // workgroup total (last exclusive prefix + last value).
 __device__ double block_excl_scan(double v, double* total) {
   __shared__ double sh_wave[kAccWaves];
   __shared__ double sh_total;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  double incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double o = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += o;
-  }
-  double excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0.0;
+  const double incl = wave_incl_scan(v);
+  double excl = wave_shift_up1(incl);
   if (lane == kWave - 1) sh_wave[wave] = incl;
   __syncthreads();
   double base = 0.0;
@@ -211,9 +252,8 @@ __device__ double block_excl_scan(double v, double* total) {
 __device__ double block_sum(double v) {
   __shared__ double sh_wave[kAccWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  if (lane == 0) sh_wave[wave] = v;
+  v = wave_incl_scan(v);
+  if (lane == kWave - 1) sh_wave[wave] = v;
   __syncthreads();
   double t = 0.0;
   if (tid == 0)
@@ -242,15 +282,9 @@ __device__ int locate_segment(const double* m, int nseg, float u, int* seg_out, 
   const int j0 = min(lane * per, nseg), j1 = min(j0 + per, nseg);
   double loc = 0.0;
   for (int j = j0; j < j1; ++j) loc += m[j];
-  double incl = loc;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double o = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += o;
-  }
-  double excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0.0;
-  const double Z = __shfl(incl, kWave - 1, kWave);
+  const double incl = wave_incl_scan(loc);
+  const double excl = wave_shift_up1(incl);
+  const double Z = wave_last(incl);
   if (!(Z > 0.0)) return 0;
   const double T = static_cast<double>(u) * Z;
   int hit = -1, lastpos = -1;
@@ -517,8 +551,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
 __device__ float block_max_all(float v) {
   __shared__ float sh_wave[kAccWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  v = wave_max(v);
   if (lane == 0) sh_wave[wave] = v;
   __syncthreads();
   float m = sh_wave[0];
