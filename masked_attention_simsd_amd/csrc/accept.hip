@@ -84,6 +84,27 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   return under ? 0.0 : ldexp(e, static_cast<int>(n));
 }
 
+// 2^(j/64), j = 0..63, each the fp64 value nearest the exact one (computed in
+// 80-digit decimal arithmetic; a CPU test recomputes and compares every entry).
+__constant__ double kExp2Frac[64] = {
+    0x1.0000000000000p+0, 0x1.02c9a3e778061p+0, 0x1.059b0d3158574p+0, 0x1.0874518759bc8p+0,
+    0x1.0b5586cf9890fp+0, 0x1.0e3ec32d3d1a2p+0, 0x1.11301d0125b51p+0, 0x1.1429aaea92de0p+0,
+    0x1.172b83c7d517bp+0, 0x1.1a35beb6fcb75p+0, 0x1.1d4873168b9aap+0, 0x1.2063b88628cd6p+0,
+    0x1.2387a6e756238p+0, 0x1.26b4565e27cddp+0, 0x1.29e9df51fdee1p+0, 0x1.2d285a6e4030bp+0,
+    0x1.306fe0a31b715p+0, 0x1.33c08b26416ffp+0, 0x1.371a7373aa9cbp+0, 0x1.3a7db34e59ff7p+0,
+    0x1.3dea64c123422p+0, 0x1.4160a21f72e2ap+0, 0x1.44e086061892dp+0, 0x1.486a2b5c13cd0p+0,
+    0x1.4bfdad5362a27p+0, 0x1.4f9b2769d2ca7p+0, 0x1.5342b569d4f82p+0, 0x1.56f4736b527dap+0,
+    0x1.5ab07dd485429p+0, 0x1.5e76f15ad2148p+0, 0x1.6247eb03a5585p+0, 0x1.6623882552225p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.6dfb23c651a2fp+0, 0x1.71f75e8ec5f74p+0, 0x1.75feb564267c9p+0,
+    0x1.7a11473eb0187p+0, 0x1.7e2f336cf4e62p+0, 0x1.82589994cce13p+0, 0x1.868d99b4492edp+0,
+    0x1.8ace5422aa0dbp+0, 0x1.8f1ae99157736p+0, 0x1.93737b0cdc5e5p+0, 0x1.97d829fde4e50p+0,
+    0x1.9c49182a3f090p+0, 0x1.a0c667b5de565p+0, 0x1.a5503b23e255dp+0, 0x1.a9e6b5579fdbfp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b33a2b84f15fbp+0, 0x1.b7f76f2fb5e47p+0, 0x1.bcc1e904bc1d2p+0,
+    0x1.c199bdd85529cp+0, 0x1.c67f12e57d14bp+0, 0x1.cb720dcef9069p+0, 0x1.d072d4a07897cp+0,
+    0x1.d5818dcfba487p+0, 0x1.da9e603db3285p+0, 0x1.dfc97337b9b5fp+0, 0x1.e502ee78b3ff6p+0,
+    0x1.ea4afa2a490dap+0, 0x1.efa1bee615a27p+0, 0x1.f50765b6e4540p+0, 0x1.fa7c1819e90d8p+0,
+};
+
 // exp(x) for x <= 0 in fp64 by table (Tang's method), for the statistics
 // pass where it runs once per logit and its instruction count sets the pass's
 // speed: x = (64 n + j) ln2/64 + r with |r| <= ln2/128 (k = 64 n + j from a
@@ -593,7 +614,7 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
       for (int e = 0; e < 4; ++e) v[4 * j + e] = y + e < V ? z[y + e] : -INFINITY;
     }
   }
-  if (tid < 64) tab[tid] = exp2(tid * (1.0 / 64.0));  // visible after the barrier in block_max_all
+  if (tid < 64) tab[tid] = kExp2Frac[tid];  // visible after the barrier in block_max_all
   float tm = -INFINITY;
 #pragma unroll
   for (int e = 0; e < PER1; ++e) tm = fmaxf(tm, v[e]);

@@ -61,3 +61,23 @@ def test_package_reexports_every_entry_point():
     assert len(wrapped) >= len(binding.EXPORTS) - 2
     for name in wrapped + ["SimsdError", "load_library", "tuning", "SIMSD_ROPE_POSITIONS"]:
         assert getattr(pkg, name) is getattr(binding, name), name
+
+
+def test_exp2_fraction_table_is_correctly_rounded():
+    # the statistics pass's table of 2^(j/64): every entry the fp64 value
+    # nearest the exact one (80-digit decimal arithmetic here)
+    import re
+    from decimal import Decimal, getcontext
+    src = open(os.path.join(ROOT, "masked_attention_simsd_amd", "csrc", "accept.hip")).read()
+    body = src[src.index("kExp2Frac[64] = {"):]
+    body = body[:body.index("};")]
+    vals = [float.fromhex(h) for h in re.findall(r"0x[0-9a-f.]+p[+-]\d+", body)]
+    assert len(vals) == 64
+    getcontext().prec = 80
+    for j, v in enumerate(vals):
+        exact = Decimal(2) ** (Decimal(j) / 64)
+        assert v == float(exact), j
+        # neither neighbouring double is closer to the exact value
+        import math
+        for nb in (math.nextafter(v, 0.0), math.nextafter(v, 4.0)):
+            assert abs(Decimal(nb) - exact) >= abs(Decimal(v) - exact), j
