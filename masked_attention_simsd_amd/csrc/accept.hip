@@ -327,8 +327,10 @@ __device__ int locate_segment(const double* m, int nseg, float u, int* seg_out, 
     src = 63 - __clzll(static_cast<long long>(pos));
     hit = lastpos, hit_base = last_base;
   }
-  *seg_out = __shfl(hit, src, kWave);
-  *base_out = __shfl(hit_base, src, kWave);
+  // src is uniform: read the lane's registers directly (no LDS permute)
+  *seg_out = __builtin_amdgcn_readlane(hit, src);
+  *base_out = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(hit_base), src),
+                               __builtin_amdgcn_readlane(__double2loint(hit_base), src));
   *T_out = T;
   return 1;
 }
@@ -338,6 +340,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   constexpr int kSeg = kAccThreads * PER;  // entries per segment / workgroup
   __shared__ int inv_s[64];
   __shared__ int sh_L, sh_stat, sh_last, sh_pick, sh_seg;
+  __shared__ int sh_wave_hit[kAccWaves], sh_wave_last[kAccWaves];
   __shared__ double sh_mass[kMaxSegments];
   __shared__ double sh_T, sh_base;
   __shared__ double sh_rs[4];  // LOGITS: row statistics of the rejected step's rows
@@ -522,8 +525,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     if (sh_seg >= 0) break;
   }
 
-  if (tid == 0) sh_pick = 0x7fffffff;
-  __syncthreads();
   const int j = sh_seg;  // < 0: no mass anywhere
   if (j >= 0) {
     const int y0 = j * kSeg + PER * tid;
@@ -541,25 +542,29 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
         if (hit < 0 && base + (excl + run) > T) hit = y0 + e;
       }
     }
-    // Entries grow with the thread index, so the pick is the hit of the
-    // lowest hitting lane of the lowest such wave: one LDS atomic per wave.
-    // (Every thread past the crossing also hits; one atomic per thread queued
-    // up to 256 of them on one LDS word, about 2 us on b8.)
+    // Entries grow with the thread index, so each wave's candidate is the hit
+    // of its lowest hitting lane (every thread past the crossing also hits)
+    // and its fallback the last positive entry of its highest such lane; one
+    // word per wave in LDS, one barrier, and thread 0 takes the first hit
+    // over the waves (rounding fallback: the last positive entry).
     const unsigned long long hits = __ballot(hit >= 0);
-    if (hits && lane == __ffsll(static_cast<long long>(hits)) - 1) atomicMin(&sh_pick, hit);
+    const unsigned long long pos = __ballot(lastpos >= 0);
+    if (lane == 0) {
+      sh_wave_hit[wave] = hits ? __builtin_amdgcn_readlane(hit, __ffsll(static_cast<long long>(hits)) - 1) : -1;
+      sh_wave_last[wave] = pos ? __builtin_amdgcn_readlane(lastpos, 63 - __clzll(static_cast<long long>(pos))) : -1;
+    }
     __syncthreads();
-    const bool none = sh_pick == 0x7fffffff;
-    __syncthreads();
-    if (none) {  // rounding: no crossing inside the segment; take its last positive entry
-      if (tid == 0) sh_pick = -1;
-      __syncthreads();
-      const unsigned long long pos = __ballot(lastpos >= 0);
-      if (pos && lane == 63 - __clzll(static_cast<long long>(pos))) atomicMax(&sh_pick, lastpos);
+    if (tid == 0) {
+      int pick = -1;
+      for (int v = kAccWaves - 1; v >= 0; --v) pick = sh_wave_hit[v] >= 0 ? sh_wave_hit[v] : pick;
+      if (pick < 0)
+        for (int v = 0; v < kAccWaves; ++v) pick = sh_wave_last[v] >= 0 ? sh_wave_last[v] : pick;
+      sh_pick = pick;
     }
   } else if (tid == 0) {
     sh_pick = -1;  // no mass at all: nothing can be drawn
   }
-  __syncthreads();
+  // thread 0 set sh_pick itself and writes the result: no barrier needed
   if (tid == 0) {
     a.accept_len[s] = L;
     a.correction[s] = sh_pick;
