@@ -43,9 +43,13 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
     const int pv = (a.next_pos && valid) ? a.pos[static_cast<size_t>(s) * B + lane] : 0;
     const bool in_range = tv >= 1 && tv <= B;
     // a permutation of 1..B: every label in range and all B label bits present
-    unsigned long long bits = (valid && in_range) ? (1ull << (tv - 1)) : 0ull;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) bits |= __shfl_xor(bits, o);
+    // (the lanes' labels read with readlane in a uniform loop: B <= 64 scalar
+    // reads, no LDS permutes)
+    unsigned long long bits = 0ull;
+    for (int t = 0; t < B; ++t) {
+      const int lt = __builtin_amdgcn_readlane(tv, t);
+      bits |= (lt >= 1 && lt <= B) ? (1ull << (lt - 1)) : 0ull;
+    }
     const unsigned long long full = B == 64 ? ~0ull : ((1ull << B) - 1ull);
     const bool perm = __ballot(valid && !in_range) == 0ull && bits == full;
     if (perm && valid) inv[tv - 1] = lane;
@@ -66,16 +70,15 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
       // then L positions following the block's largest. A sequence that
       // commits nothing keeps its block.
       int* nx = a.next_pos + static_cast<size_t>(s) * B;
-      int pmax = valid ? pv : INT_MIN;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) pmax = max(pmax, __shfl_xor(pmax, o));
-      const bool corr = valid && tv == L + 1;
-      const bool open = valid && tv > L + 1;
+      int pmax = INT_MIN;
       int rank = 0;
       for (int t = 0; t < B; ++t) {
-        const int pt = __shfl(pv, t), tt = __shfl(tv, t);
+        const int pt = __builtin_amdgcn_readlane(pv, t), tt = __builtin_amdgcn_readlane(tv, t);
+        pmax = max(pmax, pt);
         rank += (tt > L + 1 && (pt < pv || (pt == pv && t < lane))) ? 1 : 0;
       }
+      const bool corr = valid && tv == L + 1;
+      const bool open = valid && tv > L + 1;
       if (valid) {
         if (fail) {
           nx[lane] = pv;
