@@ -64,18 +64,18 @@ def test_package_reexports_every_entry_point():
 
 
 def test_exp2_fraction_table_is_correctly_rounded():
-    # the statistics pass's table of 2^(j/64): every entry the fp64 value
+    # the statistics pass's table of 2^(j/256): every entry the fp64 value
     # nearest the exact one (80-digit decimal arithmetic here)
     import re
     from decimal import Decimal, getcontext
     src = open(os.path.join(ROOT, "masked_attention_simsd_amd", "csrc", "accept.hip")).read()
-    body = src[src.index("kExp2Frac[64] = {"):]
+    body = src[src.index("kExp2Frac[256] = {"):]
     body = body[:body.index("};")]
     vals = [float.fromhex(h) for h in re.findall(r"0x[0-9a-f.]+p[+-]\d+", body)]
-    assert len(vals) == 64
+    assert len(vals) == 256
     getcontext().prec = 80
     for j, v in enumerate(vals):
-        exact = Decimal(2) ** (Decimal(j) / 64)
+        exact = Decimal(2) ** (Decimal(j) / 256)
         assert v == float(exact), j
         # neither neighbouring double is closer to the exact value
         import math
