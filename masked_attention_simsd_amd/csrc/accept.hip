@@ -195,20 +195,26 @@ __device__ __forceinline__ float softmax_prob(float z, double m, double inv_s, d
 struct RowStats {
   double mt, st, md, sd;  // st, sd: reciprocal row sums
 };
-__device__ __forceinline__ RowStats row_stats_of(const AcceptArgs& a, int s, int k) {
+// The statistics pass stores kRowStatDoubles doubles per row: (max, 1 / sum,
+// the row's logit at position k's draft token, unused); the logit slot is
+// left 0 when the draft token lies outside the vocabulary.
+constexpr int kRowStatDoubles = 4;
+__device__ __forceinline__ RowStats row_stats_of(const AcceptArgs& a, int s, int k, double* zt_x, double* zd_x) {
   const size_t rt = static_cast<size_t>(s) * a.B + k, rd = rt + static_cast<size_t>(a.b) * a.B;
-  // the statistics pass stores (max, 1 / sum)
-  return RowStats{a.row_stats[2 * rt], a.row_stats[2 * rt + 1], a.row_stats[2 * rd], a.row_stats[2 * rd + 1]};
+  const double* t = a.row_stats + kRowStatDoubles * rt;
+  const double* d = a.row_stats + kRowStatDoubles * rd;
+  *zt_x = t[2], *zd_x = d[2];
+  return RowStats{t[0], t[1], d[0], d[1]};
 }
 
-// Zero the statistics of sequence s's 2 B rows (4 B doubles, one per thread)
-// once every workgroup of the sequence has read them, so a call leaves the
-// whole workspace zero and a workspace can be reused at any other sizes.
+// Zero the statistics of sequence s's 2 B rows once every workgroup of the
+// sequence has read them, so a call leaves the whole workspace zero and a
+// workspace can be reused at any other sizes.
 __device__ __forceinline__ void clear_row_stats(const AcceptArgs& a, int s, int tid) {
-  const int n = 2 * a.B;  // doubles of one half (target or draft rows)
-  if (tid < 2 * n) {
-    const size_t half = tid < n ? 0 : static_cast<size_t>(a.b) * a.B * 2;
-    a.row_stats[half + static_cast<size_t>(s) * a.B * 2 + tid % n] = 0.0;
+  const int n = kRowStatDoubles * a.B;  // doubles of the sequence's rows in one half
+  for (int i = tid; i < 2 * n; i += kAccThreads) {
+    const size_t half = i < n ? 0 : static_cast<size_t>(a.b) * a.B * kRowStatDoubles;
+    a.row_stats[half + static_cast<size_t>(s) * n + i % n] = 0.0;
   }
 }
 
@@ -406,6 +412,12 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     // u_t of temporal step t = lane + 1, requested with tau and the drafts so
     // that its latency is not paid after the gathers
     const float u_t = lane < B ? a.u[static_cast<size_t>(s) * (B + 1) + lane] : 0.0f;
+    // LOGITS: position lane's row statistics and draft-token logits, requested
+    // with tau (none of them depends on it)
+    RowStats rs{};
+    double zt_x = 0.0, zd_x = 0.0;
+    if constexpr (LOGITS)
+      if (lane < B) rs = row_stats_of(a, s, lane, &zt_x, &zd_x);
     if (lane < B) inv_s[lane] = -1;
     // invert: position k = lane writes itself at slot tau(k) - 1; a duplicate or
     // out-of-range label makes tau invalid
@@ -421,36 +433,45 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
       }
     } else {
       const int kk = lane < B ? inv_s[lane] : 0;  // position with label lane + 1
-      const int x = __shfl(x_k, kk, kWave);
-      // LOGITS: this step's row statistics (the only reads of them in the call)
-      RowStats rs{};
-      if constexpr (LOGITS)
-        if (lane < B) rs = row_stats_of(a, s, kk);
+      // acceptance ratio min(1, p/q) at a draft token x of a row pair, and its
+      // status bits
+      auto ratio = [&](float pa, float qa, int& stat) {
+        if (qa > 0.0f) {
+          const float r = pa / qa;  // IEEE-rounded fp32 division (no fast-math in this library)
+          return r > 1.0f ? 1.0f : r;
+        }
+        stat |= kDevQZero;
+        return pa > 0.0f ? 1.0f : 0.0f;
+      };
       bool acc = true;
       int stat = 0;
-      if (lane < B) {
-        float r;
-        if (x < 0 || x >= V) {
-          stat |= kDevBadToken;
-          r = 0.0f;
+      if constexpr (LOGITS) {
+        // position lane's ratio from its own statistics, then each step takes
+        // the ratio of its position
+        int stat_k = 0;
+        float r_k = 0.0f;
+        if (x_k < 0 || x_k >= V) {
+          stat_k = kDevBadToken;
         } else {
-          const size_t at = (static_cast<size_t>(s) * B + kk) * V + x;
-          float pa, qa;
-          if constexpr (LOGITS) {
-            pa = softmax_prob(a.zt[at], rs.mt, rs.st, a.inv_t);
-            qa = softmax_prob(a.zd[at], rs.md, rs.sd, a.inv_t);
-          } else {
-            pa = a.p[at], qa = a.q[at];
-          }
-          if (qa > 0.0f) {
-            r = pa / qa;  // IEEE-rounded fp32 division (no fast-math in this library)
-            r = r > 1.0f ? 1.0f : r;
-          } else {
-            stat |= kDevQZero;
-            r = pa > 0.0f ? 1.0f : 0.0f;
-          }
+          const float pa = softmax_prob(static_cast<float>(zt_x), rs.mt, rs.st, a.inv_t);
+          const float qa = softmax_prob(static_cast<float>(zd_x), rs.md, rs.sd, a.inv_t);
+          r_k = ratio(pa, qa, stat_k);
         }
-        acc = u_t < r;
+        const float r = __shfl(r_k, kk, kWave);
+        stat = __shfl(stat_k, kk, kWave);
+        if (lane < B) acc = u_t < r;
+      } else {
+        const int x = __shfl(x_k, kk, kWave);
+        if (lane < B) {
+          float r = 0.0f;
+          if (x < 0 || x >= V) {
+            stat |= kDevBadToken;
+          } else {
+            const size_t at = (static_cast<size_t>(s) * B + kk) * V + x;
+            r = ratio(a.p[at], a.q[at], stat);
+          }
+          acc = u_t < r;
+        }
       }
       const unsigned long long rej = __ballot(lane < B && !acc);
       const int L = rej ? __ffsll(static_cast<long long>(rej)) - 1 : B;
@@ -464,7 +485,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
         sh_stat = st;
       }
       if constexpr (LOGITS) {
-        if (L < B && lane == L) {  // the rejected step's statistics, for the residual pass
+        // the rejected step's statistics (its position's lane), for the residual pass
+        if (L < B && lane == inv_s[L]) {
           sh_rs[0] = rs.mt, sh_rs[1] = rs.st, sh_rs[2] = rs.md, sh_rs[3] = rs.sd;
         }
       }
@@ -652,6 +674,7 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
   const int row = static_cast<int>(id / a.nseg1), seg = static_cast<int>(id % a.nseg1);
   const int V = a.V, tid = threadIdx.x;
   const float* z = (row < nrow_half ? a.zt : a.zd) + static_cast<size_t>(row % nrow_half) * V;
+  const int xdraft = a.draft[row % nrow_half];  // the draft token of the row's position
   // thread tid takes the 4-entry pieces seg SEG1 + 4 (tid + 256 j): each load
   // instruction of a wave reads 1 KB of contiguous logits
   const int y0 = seg * SEG1 + 4 * tid;
@@ -669,6 +692,17 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
     }
   }
   tab[tid] = kExp2Frac[tid];  // visible after the barrier in block_max_all
+  // The workgroup whose segment holds the draft token leaves the logit there
+  // beside the row's statistics, so the acceptance pass reads it together
+  // with them instead of gathering it.
+  const int xoff = xdraft - seg * SEG1;
+  if (xoff >= 0 && xoff < SEG1 && xdraft < V && tid == (xoff % (4 * kAccThreads)) / 4) {
+    float zx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER1; ++e)
+      if ((e / 4) * 4 * kAccThreads + (e % 4) == xoff - 4 * tid) zx = v[e];
+    a.row_stats[kRowStatDoubles * static_cast<size_t>(row) + 2] = static_cast<double>(zx);
+  }
   float tm = -INFINITY;
 #pragma unroll
   for (int e = 0; e < PER1; ++e) tm = fmaxf(tm, v[e]);
@@ -750,8 +784,8 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
   const double S = block_sum(part);
   if (timed_out && a.status) atomicOr(&a.status[(row % nrow_half) / a.B], kDevSyncTimeout);
   if (tid == 0) {
-    a.row_stats[2 * static_cast<size_t>(row)] = static_cast<double>(M);
-    a.row_stats[2 * static_cast<size_t>(row) + 1] = 1.0 / S;
+    a.row_stats[kRowStatDoubles * static_cast<size_t>(row)] = static_cast<double>(M);
+    a.row_stats[kRowStatDoubles * static_cast<size_t>(row) + 1] = 1.0 / S;
     __hip_atomic_store(row_counter(a, row), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -402,8 +402,9 @@ size_t simsd_accept_logits_workspace(int b, int B, int V) {
   // row counters 128 bytes apart for up to 2048 rows (the row-statistics
   // kernel indexes them with the same rule), packed beyond that
   const long row_stride = rows <= 2048 ? 32 : 1;
+  // per row: (max, 1 / sum, logit at the draft token, unused)
   return base + up(rows * row_stride * sizeof(int32_t)) + up(rows * nseg1 * 2 * sizeof(uint64_t)) +
-         up(rows * 2 * sizeof(double));
+         up(rows * 4 * sizeof(double));
 }
 
 int simsd_accept_logits(const float* target_logits, const float* draft_logits, float temperature,

@@ -171,7 +171,7 @@ struct AcceptArgs {
   // statistics (max, sum of exp) the row-statistics pass leaves in row_stats.
   const float* zt;
   const float* zd;
-  double* row_stats;              // [2][b][B] x (max, 1 / sum): target rows, then draft rows
+  double* row_stats;              // [2][b][B] x (max, 1 / sum, logit at the draft token, 0): target rows, then draft rows
   double inv_t;
   int32_t* row_counters;          // [2 b B], zero between calls
   unsigned long long* row_words;  // [2 b B][nseg1] x (max, sum) with ready bits, zero between calls
