@@ -163,18 +163,22 @@ __constant__ double kExp2Frac[256] = {
 // uses ln2/256 as one double: r is off by at most |x| 2^-53, so a term e^x
 // carries a relative error of about |x| 1.1e-16 on top of a few 1e-16, and
 // its share of a row sum's error, e^x |x| 1.1e-16 <= 0.37 * 1.1e-16 per unit
-// of the sum, stays at the rounding level of the sum itself. x is first
+// of the sum, stays at the rounding level of the sum itself. With TWO_PART
+// the reduction takes ln2/256 in two parts (one more fma) and the error is a
+// few 1e-16 at every x, for probabilities evaluated one by one. x is first
 // clamped to [-708, 0] (NaN as well): below that the true value is under
 // 3.4e-308 and the result, 3.3e-308, is equally invisible in a row sum of at
 // least 1 (it keeps n >= -1022 with T[j](1 + p) >= 1, so the scaled result
-// stays normal).
+// stays normal); a probability that small rounds to 0 in fp32 either way.
+template <bool TWO_PART = false>
 __device__ __forceinline__ double exp_nonpos_tab(double x, const double* tab) {
   x = fmax(x, -708.0);
   constexpr double kShift = 6755399441055744.0;  // 1.5 * 2^52: k lands in the low word
   const double kt = __builtin_fma(x, 369.3299304675746, kShift);  // x * 256 / ln2 + shift
   const int k = __double2loint(kt);
   const double kd = kt - kShift;
-  const double r = __builtin_fma(-kd, 0x1.62e42fefa39efp-9, x);  // ln2/256
+  double r = __builtin_fma(-kd, 0x1.62e42fefa39efp-9, x);  // ln2/256 (its high part with TWO_PART)
+  if constexpr (TWO_PART) r = __builtin_fma(-kd, 0x1.abc9e3b39803fp-64, r);  // ln2/256, low part
   double p = 1.0 / 24.0;
   p = __builtin_fma(p, r, 1.0 / 6.0);
   p = __builtin_fma(p, r, 0.5);
@@ -189,6 +193,12 @@ __device__ __forceinline__ double exp_nonpos_tab(double x, const double* tab) {
 // in fp64, rounded once to fp32 (the precision the decisions are taken in).
 __device__ __forceinline__ float softmax_prob(float z, double m, double inv_s, double inv_t) {
   return static_cast<float>(exp_nonpos((static_cast<double>(z) - m) * inv_t) * inv_s);
+}
+// The same with the table exponential (two-part reduction), for the residual
+// rows where every thread evaluates a few of them per entry it holds.
+__device__ __forceinline__ float softmax_prob_tab(float z, double m, double inv_s, double inv_t,
+                                                  const double* tab) {
+  return static_cast<float>(exp_nonpos_tab<true>((static_cast<double>(z) - m) * inv_t, tab) * inv_s);
 }
 
 // Row statistics of the target and draft rows (s, k): (max, 1 / sum of exp).
@@ -224,7 +234,7 @@ __device__ __forceinline__ void clear_row_stats(const AcceptArgs& a, int s, int 
 template <int PER, bool LOGITS>
 __device__ __forceinline__ void load_masses(const float* prow, const float* qrow, int y0, int V,
                                             bool vec, bool use_p, const RowStats& rs, double inv_t,
-                                            float (&w)[PER]) {
+                                            const double* tab, float (&w)[PER]) {
   float pv[PER], qv[PER];
   if (vec && y0 + PER <= V) {
 #pragma unroll
@@ -245,8 +255,8 @@ __device__ __forceinline__ void load_masses(const float* prow, const float* qrow
   if constexpr (LOGITS) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      pv[e] = softmax_prob(pv[e], rs.mt, rs.st, inv_t);
-      qv[e] = use_p ? 0.0f : softmax_prob(qv[e], rs.md, rs.sd, inv_t);
+      pv[e] = softmax_prob_tab(pv[e], rs.mt, rs.st, inv_t, tab);
+      qv[e] = use_p ? 0.0f : softmax_prob_tab(qv[e], rs.md, rs.sd, inv_t, tab);
     }
   }
 #pragma unroll
@@ -399,12 +409,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   __shared__ double sh_mass[kMaxSegments];
   __shared__ double sh_T, sh_base;
   __shared__ double sh_rs[4];  // LOGITS: row statistics of the rejected step's rows
+  __shared__ double exp_tab[LOGITS ? 256 : 1];  // LOGITS: 2^(j/256) for the residual rows
 
   const int seg = blockIdx.x, nseg = gridDim.x;
   const int s = blockIdx.y;
   const int B = a.B, V = a.V;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const float u_corr = a.u[static_cast<size_t>(s) * (B + 1) + B];  // requested early
+  if constexpr (LOGITS) exp_tab[tid] = kExp2Frac[tid];  // read after the first barrier
 
   if (wave == 0) {
     const int t_k = lane < B ? a.tau[static_cast<size_t>(s) * B + lane] : 0;  // tau(lane+1)
@@ -526,7 +538,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   // ---- every workgroup: residual mass of its segment, published with the
   // ready bit; the arrival counter moves without waiting for the publish ----
   float w[PER];
-  load_masses<PER, LOGITS>(prow, qrow, seg * kSeg + PER * tid, V, vec, false, rs, a.inv_t, w);
+  load_masses<PER, LOGITS>(prow, qrow, seg * kSeg + PER * tid, V, vec, false, rs, a.inv_t, exp_tab, w);
   const double mine = block_sum(thread_sum<PER>(w));
   unsigned long long* words = reinterpret_cast<unsigned long long*>(a.seg_sum) +
                               static_cast<size_t>(s) * nseg;
@@ -571,7 +583,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     if (use_p) {  // zero residual: the (rare) fallback draws from p; masses of p, all segments here
       for (int j = 0; j < nseg; ++j) {
         float wp[PER];
-        load_masses<PER, LOGITS>(prow, qrow, j * kSeg + PER * tid, V, vec, true, rs, a.inv_t, wp);
+        load_masses<PER, LOGITS>(prow, qrow, j * kSeg + PER * tid, V, vec, true, rs, a.inv_t, exp_tab, wp);
         const double m = block_sum(thread_sum<PER>(wp));
         if (tid == 0) sh_mass[j] = m;
       }
@@ -599,7 +611,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   const int j = sh_seg;  // < 0: no mass anywhere
   if (j >= 0) {
     const int y0 = j * kSeg + PER * tid;
-    if (j != seg || use_p) load_masses<PER, LOGITS>(prow, qrow, y0, V, vec, use_p, rs, a.inv_t, w);
+    if (j != seg || use_p) load_masses<PER, LOGITS>(prow, qrow, y0, V, vec, use_p, rs, a.inv_t, exp_tab, w);
     double total;
     const double excl = block_excl_scan(thread_sum<PER>(w), &total);
     const double T = sh_T, base = sh_base;
