@@ -58,32 +58,6 @@ __device__ __forceinline__ int* row_counter(const AcceptArgs& a, int row) {
   return a.row_counters + static_cast<size_t>(row) * (rows <= 2048 ? 32 : 1);
 }
 
-// exp(x) for x <= 0 in fp64, relative error below 1e-14: Cody-Waite
-// reduction x = n ln2 + r with the two-part ln 2 of fdlibm (|r| <= ln2 / 2),
-// the Taylor series of e^r to degree 11 (truncation < 7e-15 there), and an
-// exponent scale by 2^n. Arguments below -708 give 0 (the softmax terms
-// they stand for are below fp64's normal range; the fp32 probabilities are 0).
-__device__ __forceinline__ double exp_nonpos(double x) {
-  const bool under = !(x > -708.0);  // branch-free: the result is selected at the end
-  x = under ? 0.0 : x;
-  const double n = rint(x * 1.4426950408889634);
-  double r = __builtin_fma(-n, 6.93147180369123816490e-01, x);
-  r = __builtin_fma(-n, 1.90821492927058770002e-10, r);
-  double e = 1.0 / 39916800.0;  // 1/11!
-  e = __builtin_fma(e, r, 1.0 / 3628800.0);
-  e = __builtin_fma(e, r, 1.0 / 362880.0);
-  e = __builtin_fma(e, r, 1.0 / 40320.0);
-  e = __builtin_fma(e, r, 1.0 / 5040.0);
-  e = __builtin_fma(e, r, 1.0 / 720.0);
-  e = __builtin_fma(e, r, 1.0 / 120.0);
-  e = __builtin_fma(e, r, 1.0 / 24.0);
-  e = __builtin_fma(e, r, 1.0 / 6.0);
-  e = __builtin_fma(e, r, 0.5);
-  e = __builtin_fma(e, r, 1.0);
-  e = __builtin_fma(e, r, 1.0);
-  return under ? 0.0 : ldexp(e, static_cast<int>(n));
-}
-
 // 2^(j/256), j = 0..255, each the fp64 value nearest the exact one (computed
 // in 80-digit decimal arithmetic; a CPU test recomputes and compares every
 // entry).
@@ -190,12 +164,8 @@ __device__ __forceinline__ double exp_nonpos_tab(double x, const double* tab) {
 
 // Softmax probability of logit z in a row with statistics (max m, sum of
 // exp s, passed as 1/s) at inverse temperature inv_t: exp((z - m) inv_t) / s
-// in fp64, rounded once to fp32 (the precision the decisions are taken in).
-__device__ __forceinline__ float softmax_prob(float z, double m, double inv_s, double inv_t) {
-  return static_cast<float>(exp_nonpos((static_cast<double>(z) - m) * inv_t) * inv_s);
-}
-// The same with the table exponential (two-part reduction), for the residual
-// rows where every thread evaluates a few of them per entry it holds.
+// in fp64 (table exponential with the two-part reduction), rounded once to
+// fp32 (the precision the decisions are taken in).
 __device__ __forceinline__ float softmax_prob_tab(float z, double m, double inv_s, double inv_t,
                                                   const double* tab) {
   return static_cast<float>(exp_nonpos_tab<true>((static_cast<double>(z) - m) * inv_t, tab) * inv_s);
@@ -416,9 +386,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   const int B = a.B, V = a.V;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const float u_corr = a.u[static_cast<size_t>(s) * (B + 1) + B];  // requested early
-  if constexpr (LOGITS) exp_tab[tid] = kExp2Frac[tid];  // read after the first barrier
-
   if (wave == 0) {
+    // LOGITS: wave 0 stages the exponential's table (its own ratios read it
+    // before the first barrier, the other waves after it); requested first,
+    // written to LDS once the loads below are in flight
+    double tab_v[LOGITS ? 256 / kWave : 1];
+    if constexpr (LOGITS)
+#pragma unroll
+      for (int j = 0; j < 256 / kWave; ++j) tab_v[j] = kExp2Frac[lane + j * kWave];
     const int t_k = lane < B ? a.tau[static_cast<size_t>(s) * B + lane] : 0;  // tau(lane+1)
     const int x_k = lane < B ? a.draft[static_cast<size_t>(s) * B + lane] : 0;
     // u_t of temporal step t = lane + 1, requested with tau and the drafts so
@@ -428,8 +403,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     // with tau (none of them depends on it)
     RowStats rs{};
     double zt_x = 0.0, zd_x = 0.0;
-    if constexpr (LOGITS)
+    if constexpr (LOGITS) {
       if (lane < B) rs = row_stats_of(a, s, lane, &zt_x, &zd_x);
+#pragma unroll
+      for (int j = 0; j < 256 / kWave; ++j) exp_tab[lane + j * kWave] = tab_v[j];
+    }
     if (lane < B) inv_s[lane] = -1;
     // invert: position k = lane writes itself at slot tau(k) - 1; a duplicate or
     // out-of-range label makes tau invalid
@@ -465,8 +443,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
         if (x_k < 0 || x_k >= V) {
           stat_k = kDevBadToken;
         } else {
-          const float pa = softmax_prob(static_cast<float>(zt_x), rs.mt, rs.st, a.inv_t);
-          const float qa = softmax_prob(static_cast<float>(zd_x), rs.md, rs.sd, a.inv_t);
+          const float pa = softmax_prob_tab(static_cast<float>(zt_x), rs.mt, rs.st, a.inv_t, exp_tab);
+          const float qa = softmax_prob_tab(static_cast<float>(zd_x), rs.md, rs.sd, a.inv_t, exp_tab);
           r_k = ratio(pa, qa, stat_k);
         }
         const float r = __shfl(r_k, kk, kWave);
@@ -792,7 +770,7 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
 #pragma unroll
   for (int i = 0; i < kMaxSegPerThread; ++i)
     if (tid + i * kAccThreads < a.nseg1)
-      part += sj[i] * exp_nonpos((static_cast<double>(mj[i]) - static_cast<double>(M)) * a.inv_t);
+      part += sj[i] * exp_nonpos_tab<true>((static_cast<double>(mj[i]) - static_cast<double>(M)) * a.inv_t, tab);
   const double S = block_sum(part);
   if (timed_out && a.status) atomicOr(&a.status[(row % nrow_half) / a.B], kDevSyncTimeout);
   if (tid == 0) {
