@@ -334,8 +334,10 @@ size_t simsd_accept_workspace(int b, int B, int V);
  * q = softmax(draft_logits / T), row-wise over the vocabulary, with the
  * softmax evaluated where it is needed instead of materialised: one pass
  * over all 2 b B rows finds each row's maximum and sum of exponentials
- * (fp64), then the acceptance kernel evaluates p and q at the draft tokens
+ * (fp64), then the acceptance step evaluates p and q at the draft tokens
  * and over the rejected position's row (fp64 exp, one rounding to fp32).
+ * Large batches run both in one launch (each sequence's acceptance starts
+ * once its rows' statistics are published), small ones in two.
  * The temperature is this library's reading (the pages do not define one for
  * SimSD); T = 1 gives the plain softmax.
  *

@@ -175,26 +175,60 @@ __device__ __forceinline__ float softmax_prob_tab(float z, double m, double inv_
 struct RowStats {
   double mt, st, md, sd;  // st, sd: reciprocal row sums
 };
-// The statistics pass stores kRowStatDoubles doubles per row: (max, 1 / sum,
-// the row's logit at position k's draft token, unused); the logit slot is
-// left 0 when the draft token lies outside the vocabulary.
-constexpr int kRowStatDoubles = 4;
-__device__ __forceinline__ RowStats row_stats_of(const AcceptArgs& a, int s, int k, double* zt_x, double* zd_x) {
+// The statistics pass publishes kRowStatWords 64-bit words per row, each
+// with the ready bit: the row maximum (float bits), 1 / sum (a positive
+// double, so its sign bit is free), the row's logit at position k's draft
+// token (float bits; never written when that token lies outside the
+// vocabulary) and an unused word. Readers poll them, so they may run in the
+// same launch as the pass.
+constexpr int kRowStatWords = 4;
+__device__ __forceinline__ unsigned long long* row_stat_words(const AcceptArgs& a, size_t row) {
+  return reinterpret_cast<unsigned long long*>(a.row_stats) + kRowStatWords * row;
+}
+__device__ __forceinline__ void publish_word(unsigned long long* w, unsigned long long bits) {
+  __hip_atomic_store(w, bits | kReady, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Statistics of position k of sequence s (target and draft rows) and, when the
+// draft token is in the vocabulary, its two logits; waits (bounded) until they
+// are published. Returns false if a wait ran out.
+__device__ __forceinline__ bool row_stats_of(const AcceptArgs& a, int s, int k, bool with_logits, RowStats* rs,
+                                             double* zt_x, double* zd_x) {
   const size_t rt = static_cast<size_t>(s) * a.B + k, rd = rt + static_cast<size_t>(a.b) * a.B;
-  const double* t = a.row_stats + kRowStatDoubles * rt;
-  const double* d = a.row_stats + kRowStatDoubles * rd;
-  *zt_x = t[2], *zd_x = d[2];
-  return RowStats{t[0], t[1], d[0], d[1]};
+  const unsigned long long* t = row_stat_words(a, rt);
+  const unsigned long long* d = row_stat_words(a, rd);
+  unsigned long long w[6];
+  bool ok = false;
+  int polls = 0;
+  do {
+    w[0] = __hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[1] = __hip_atomic_load(t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[2] = __hip_atomic_load(t + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[3] = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[4] = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[5] = __hip_atomic_load(d + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ok = (w[0] & w[1] & w[3] & w[4] & kReady) && (!with_logits || (w[2] & w[5] & kReady));
+    if (ok) break;
+    __builtin_amdgcn_s_sleep(2);
+  } while (++polls < kPollLimit);
+  *rs = RowStats{static_cast<double>(__uint_as_float(static_cast<uint32_t>(w[0]))),
+                 __longlong_as_double(static_cast<long long>(w[1] & ~kReady)),
+                 static_cast<double>(__uint_as_float(static_cast<uint32_t>(w[3]))),
+                 __longlong_as_double(static_cast<long long>(w[4] & ~kReady))};
+  *zt_x = static_cast<double>(__uint_as_float(static_cast<uint32_t>(w[2])));
+  *zd_x = static_cast<double>(__uint_as_float(static_cast<uint32_t>(w[5])));
+  return ok;
 }
 
 // Zero the statistics of sequence s's 2 B rows once every workgroup of the
 // sequence has read them, so a call leaves the whole workspace zero and a
 // workspace can be reused at any other sizes.
 __device__ __forceinline__ void clear_row_stats(const AcceptArgs& a, int s, int tid) {
-  const int n = kRowStatDoubles * a.B;  // doubles of the sequence's rows in one half
+  const int n = kRowStatWords * a.B;  // words of the sequence's rows in one half
+  unsigned long long* w = row_stat_words(a, 0);
   for (int i = tid; i < 2 * n; i += kAccThreads) {
-    const size_t half = i < n ? 0 : static_cast<size_t>(a.b) * a.B * kRowStatDoubles;
-    a.row_stats[half + static_cast<size_t>(s) * n + i % n] = 0.0;
+    const size_t half = i < n ? 0 : static_cast<size_t>(a.b) * a.B * kRowStatWords;
+    __hip_atomic_store(w + half + static_cast<size_t>(s) * n + i % n, 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -371,18 +405,16 @@ __device__ int locate_segment(const double* m, int nseg, float u, int* seg_out, 
 }
 
 template <int PER, bool LOGITS>
-__global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
+__device__ __forceinline__ void accept_body(const AcceptArgs& a, const int seg, const int nseg, const int s,
+                                            double* sh_mass) {
   constexpr int kSeg = kAccThreads * PER;  // entries per segment / workgroup
   __shared__ int inv_s[64];
   __shared__ int sh_L, sh_stat, sh_last, sh_pick, sh_seg;
   __shared__ int sh_wave_hit[kAccWaves], sh_wave_last[kAccWaves];
-  __shared__ double sh_mass[kMaxSegments];
   __shared__ double sh_T, sh_base;
   __shared__ double sh_rs[4];  // LOGITS: row statistics of the rejected step's rows
   __shared__ double exp_tab[LOGITS ? 256 : 1];  // LOGITS: 2^(j/256) for the residual rows
 
-  const int seg = blockIdx.x, nseg = gridDim.x;
-  const int s = blockIdx.y;
   const int B = a.B, V = a.V;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const float u_corr = a.u[static_cast<size_t>(s) * (B + 1) + B];  // requested early
@@ -403,8 +435,9 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     // with tau (none of them depends on it)
     RowStats rs{};
     double zt_x = 0.0, zd_x = 0.0;
+    bool stats_ok = true;
     if constexpr (LOGITS) {
-      if (lane < B) rs = row_stats_of(a, s, lane, &zt_x, &zd_x);
+      if (lane < B) stats_ok = row_stats_of(a, s, lane, x_k >= 0 && x_k < V, &rs, &zt_x, &zd_x);
 #pragma unroll
       for (int j = 0; j < 256 / kWave; ++j) exp_tab[lane + j * kWave] = tab_v[j];
     }
@@ -470,6 +503,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
       int st = 0;
       if (__ballot(seen && (stat & kDevBadToken))) st |= kDevBadToken;
       if (__ballot(seen && (stat & kDevQZero))) st |= kDevQZero;
+      if (__ballot(!stats_ok)) st |= kDevSyncTimeout;
       if (lane == 0) {
         sh_L = L;
         sh_stat = st;
@@ -655,12 +689,15 @@ __device__ float block_max_all(float v) {
 // collects them, folds S = sum_j s_j exp((m_j - M) / T) with M = max_j m_j in a
 // fixed order, writes (M, S) and clears its words and counter.
 template <int PER1, bool UNIT_T>
-__global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
+__device__ __forceinline__ void row_stats_body(const AcceptArgs& a, const long id) {
   constexpr int SEG1 = PER1 * kAccThreads;
   __shared__ int sh_last;
   __shared__ double tab[256];  // 2^(j/256)
   const int nrow_half = a.b * a.B;
-  const long id = blockIdx.x;
+  // rows in storage order: every target row, then every draft row, so a
+  // sequence's statistics are complete once its draft rows are, through the
+  // second half of the pass (taking each sequence's 2 B rows together made
+  // the pass 0.8-2.5 us slower)
   const int row = static_cast<int>(id / a.nseg1), seg = static_cast<int>(id % a.nseg1);
   const int V = a.V, tid = threadIdx.x;
   const float* z = (row < nrow_half ? a.zt : a.zd) + static_cast<size_t>(row % nrow_half) * V;
@@ -691,7 +728,7 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
 #pragma unroll
     for (int e = 0; e < PER1; ++e)
       if ((e / 4) * 4 * kAccThreads + (e % 4) == xoff - 4 * tid) zx = v[e];
-    a.row_stats[kRowStatDoubles * static_cast<size_t>(row) + 2] = static_cast<double>(zx);
+    publish_word(row_stat_words(a, row) + 2, __float_as_uint(zx));
   }
   float tm = -INFINITY;
 #pragma unroll
@@ -774,10 +811,39 @@ __global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
   const double S = block_sum(part);
   if (timed_out && a.status) atomicOr(&a.status[(row % nrow_half) / a.B], kDevSyncTimeout);
   if (tid == 0) {
-    a.row_stats[kRowStatDoubles * static_cast<size_t>(row)] = static_cast<double>(M);
-    a.row_stats[kRowStatDoubles * static_cast<size_t>(row) + 1] = 1.0 / S;
+    publish_word(row_stat_words(a, row), __float_as_uint(M));
+    publish_word(row_stat_words(a, row) + 1, static_cast<unsigned long long>(__double_as_longlong(1.0 / S)));
     __hip_atomic_store(row_counter(a, row), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+template <int PER, bool LOGITS>
+__global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
+  extern __shared__ double dyn_mass[];  // one mass per segment
+  accept_body<PER, LOGITS>(a, blockIdx.x, gridDim.x, blockIdx.y, dyn_mass);
+}
+
+template <int PER1, bool UNIT_T>
+__global__ __launch_bounds__(kAccThreads) void row_stats_kernel(AcceptArgs a) {
+  row_stats_body<PER1, UNIT_T>(a, blockIdx.x);
+}
+
+// Acceptance from logits in one launch: the first `units` workgroups compute
+// the row statistics, the rest (one per (sequence, segment)) run acceptance,
+// each waiting (bounded) for its sequence's statistics. Workgroups are
+// dispatched in id order, so every statistics workgroup has been dispatched
+// before an acceptance workgroup can start waiting for it, and the waits end.
+template <int PER1, bool UNIT_T, int PER>
+__global__ __launch_bounds__(kAccThreads) void accept_logits_kernel(
+    AcceptArgs a, long units, int nseg) {
+  extern __shared__ double dyn_mass[];
+  const long id = blockIdx.x;
+  if (id < units) {
+    row_stats_body<PER1, UNIT_T>(a, id);
+    return;
+  }
+  const long k = id - units;
+  accept_body<PER, true>(a, static_cast<int>(k % nseg), nseg, static_cast<int>(k / nseg), dyn_mass);
 }
 
 // Entries per thread (segment width / 256): 4 (1024-entry segments). With
@@ -802,12 +868,13 @@ hipError_t launch_accept_mode(const AcceptArgs& a, hipStream_t stream) {
   const int per = accept_per(a.b, a.V);
   const int nseg = (a.V + kAccThreads * per - 1) / (kAccThreads * per);
   dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(a.b));
+  const size_t dyn = static_cast<size_t>(nseg) * sizeof(double);
   if (per == 4)
-    hipLaunchKernelGGL((accept_kernel<4, LOGITS>), grid, dim3(kAccThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_kernel<4, LOGITS>), grid, dim3(kAccThreads), dyn, stream, a);
   else if (per == 8)
-    hipLaunchKernelGGL((accept_kernel<8, LOGITS>), grid, dim3(kAccThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_kernel<8, LOGITS>), grid, dim3(kAccThreads), dyn, stream, a);
   else
-    hipLaunchKernelGGL((accept_kernel<16, LOGITS>), grid, dim3(kAccThreads), 0, stream, a);
+    hipLaunchKernelGGL((accept_kernel<16, LOGITS>), grid, dim3(kAccThreads), dyn, stream, a);
   return hipGetLastError();
 }
 
@@ -822,6 +889,18 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) { return launc
 // 32768 with 1024 rows -> 37.6 / 41.0 / 42.2 us; a variant streaming longer
 // runs with prefetch measured 42.9 us on the first). The tuning override
 // SIMSD_TUNE_ROWSTAT_PER = 16, 32 or 64 replaces the default.
+// Statistics and acceptance go in one launch when the statistics grid takes
+// at least two rounds of resident workgroups (MI355X: 256 CUs x 8), so that
+// the acceptance of the sequences done early overlaps the rest of the
+// statistics; a grid that fits one round gains no overlap, and the waiting
+// acceptance workgroups cost it. Interleaved runs (event pairs, logits copies
+// rotated past the MALL), two launches -> one: b = 64 B = 8 V = 32768
+// 51.7 -> 47.7 us, b = 8 B = 16 V = 151936 53.7 -> 53.3 us; with the rows
+// in sequence order (which slowed the pass itself) also b = 16 B = 16 V =
+// 151936 91.4 -> 88.4, b = 32 B = 8 V = 32768 35.0 -> 32.8, b = 32 B = 4
+// V = 65536 37.2 -> 32.6, b = 4 B = 16 V = 151936 37.1 -> 36.5, but b = 16
+// B = 8 V = 32768 (2048 statistics workgroups, one round) 25.1 -> 26.4.
+constexpr long kOneLaunchMinRowStatUnits = 2L * 256 * 8;
 int row_stat_per() {
   const int forced = tuning(SIMSD_TUNE_ROWSTAT_PER);
   return (forced == 16 || forced == 32 || forced == 64) ? forced : 16;
@@ -835,6 +914,18 @@ hipError_t launch_accept_logits(const AcceptArgs& a0, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(units)), block(kAccThreads);
   // T = 1 (inverse temperature exactly 1) skips a multiply per logit
   const bool unit = a.inv_t == 1.0;
+  const int per = accept_per(a.b, a.V);
+  if (units >= kOneLaunchMinRowStatUnits && per1 == 16 && per == 4) {
+    // the default widths: statistics and acceptance in one launch
+    const int nseg = (a.V + kAccThreads * per - 1) / (kAccThreads * per);
+    const dim3 g1(static_cast<unsigned>(units + static_cast<long>(nseg) * a.b));
+    const size_t dyn = static_cast<size_t>(nseg) * sizeof(double);
+    if (unit)
+      hipLaunchKernelGGL((accept_logits_kernel<16, true, 4>), g1, block, dyn, stream, a, units, nseg);
+    else
+      hipLaunchKernelGGL((accept_logits_kernel<16, false, 4>), g1, block, dyn, stream, a, units, nseg);
+    return hipGetLastError();
+  }
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
   if (per1 == 16)
     unit ? go(row_stats_kernel<16, true>) : go(row_stats_kernel<16, false>);

@@ -117,6 +117,29 @@ def test_edge_cases():
           rng.random((3, 3)).astype(np.float32), 1.0, "V=1")
 
 
+def test_one_launch_edge_cases():
+    # 2 b B V / 4096 >= 4096 statistics workgroups: statistics and acceptance
+    # run in one launch, the acceptance waiting for its sequence's published
+    # statistics. A draft id outside the vocabulary has no logit word to wait
+    # for; a bad tau, a one-hot q and p == q take their usual paths; the
+    # workspace is left zero for the next call.
+    V, b, B = 32768, 32, 8
+    zt, zd, draft, tau, u = random_logits(V, b, B, seed=11)
+    tau[0, :2] = 1  # not a permutation
+    draft[1, np.argsort(tau[1])[0]] = V + 3  # draft id out of range at step 1
+    draft[2, np.argsort(tau[2])[2]] = -1  # out of range at step 3
+    k = np.argsort(tau[3])[0]
+    zd[3, k, :] = -1e30
+    zd[3, k, draft[3, k]] = 0.0  # q one-hot at the draft, p(x) < 1: residual draw from p
+    zd[4] = zt[4]  # p == q: every step accepted
+    need = binding.simsd_accept_logits_workspace(b, B, V)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        L, corr = check(zt, zd, draft, tau, u, 1.0, f"one launch, status cases {rep}", ws=ws)
+        assert L[4] == B and corr[4] == -1
+        assert int(torch.count_nonzero(ws)) == 0
+
+
 @pytest.mark.parametrize("V,b,per", [(151936, 8, 16), (151936, 8, 64), (20480, 16, 64), (12289, 4, 16),
                                      (4097, 32, 64)])
 def test_row_statistics_segment_widths(V, b, per):
