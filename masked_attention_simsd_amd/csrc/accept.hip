@@ -37,7 +37,6 @@ namespace {
 constexpr int kAccThreads = 256;
 constexpr int kAccWaves = kAccThreads / kWave;
 constexpr int kMinPer = 4;  // smallest entries-per-thread variant (sizes the workspace)
-constexpr int kMaxSegments = kMaxAcceptVocab / (kAccThreads * kMinPer);
 // A published segment mass carries this bit (masses are +0 or positive, so
 // the sign bit is free); a cleared word (0) means "not yet published".
 constexpr unsigned long long kReady = 1ull << 63;
