@@ -25,6 +25,13 @@
 //   scan over the segment masses, and rescans that segment with a
 //   workgroup-wide prefix sum for the first token whose running mass exceeds T.
 // Traffic: 2 V fp32 per rejecting sequence plus one segment re-read.
+//
+// From logits (simsd_accept_logits) a row-statistics pass first reduces every
+// target and draft row to its maximum and sum of exponentials and publishes
+// them, with the logit at the row's draft token, as ready-bit words; phase 1
+// then reads a position's ratio inputs from those words instead of gathering,
+// and phase 2 evaluates p and q from the logits of the rejected rows. Large
+// batches run the pass and the acceptance in one grid (accept_logits_kernel).
 #include "simsd.h"
 #include "simsd_internal.h"
 
