@@ -140,6 +140,33 @@ def test_one_launch_edge_cases():
         assert int(torch.count_nonzero(ws)) == 0
 
 
+def _one_launch_shapes(n, seed):
+    # random (b, B, V, T) whose statistics grid, 2 b B ceil(V / 4096)
+    # workgroups, is at least 4096 (the one-launch form), logits <= 96 MB
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        b = int(rng.integers(1, 65))
+        B = int(rng.choice([1, 3, 8, 16, 33, 64]))
+        V = int(rng.integers(1000, 200000))
+        units = 2 * b * B * -(-V // 4096)
+        if units >= 4096 and 2 * b * B * V * 4 <= 96 << 20:
+            out.append((b, B, V, float(rng.choice([0.5, 1.0, 1.3]))))
+    return out
+
+
+@pytest.mark.parametrize("b,B,V,T", _one_launch_shapes(8, 2026))
+def test_one_launch_random_shapes(b, B, V, T):
+    # statistics and acceptance in one launch over random batch, block and
+    # vocabulary sizes (ragged last segments included); the workspace is left
+    # zero after each call
+    say(f"one launch b={b} B={B} V={V} T={T}")
+    need = binding.simsd_accept_logits_workspace(b, B, V)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    check(*random_logits(V, b, B, seed=b * 1000 + B + V), T, f"one launch b={b} B={B} V={V}", ws=ws)
+    assert int(torch.count_nonzero(ws)) == 0
+
+
 @pytest.mark.parametrize("V,b,per", [(151936, 8, 16), (151936, 8, 64), (20480, 16, 64), (12289, 4, 16),
                                      (4097, 32, 64)])
 def test_row_statistics_segment_widths(V, b, per):
