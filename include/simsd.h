@@ -356,7 +356,7 @@ size_t simsd_accept_workspace(int b, int B, int V);
  * a uniform lies within a few fp32 ulps of its step's ratio, or u_{B+1} * Z
  * within rounding of a CDF step (the exponentials are evaluated in another
  * order than a sequential softmax).
- * Errors: SIMSD_ERR_NULL, _SIZE (as simsd_accept; also 2 b B ceil(V/4096) >
+ * Errors: SIMSD_ERR_NULL, _SIZE (as simsd_accept; also 2 b B ceil(V/4096) >=
  * 2^24), _SCALE, _ALIGN, _WORKSPACE, _LAUNCH.
  */
 int simsd_accept_logits(const float* target_logits, const float* draft_logits, float temperature,

@@ -921,10 +921,12 @@ hipError_t launch_accept_logits(const AcceptArgs& a0, hipStream_t stream) {
   // T = 1 (inverse temperature exactly 1) skips a multiply per logit
   const bool unit = a.inv_t == 1.0;
   const int per = accept_per(a.b, a.V);
-  if (units >= kOneLaunchMinRowStatUnits && per1 == 16 && per == 4) {
-    // the default widths: statistics and acceptance in one launch
-    const int nseg = (a.V + kAccThreads * per - 1) / (kAccThreads * per);
-    const dim3 g1(static_cast<unsigned>(units + static_cast<long>(nseg) * a.b));
+  const int nseg = (a.V + kAccThreads * per - 1) / (kAccThreads * per);
+  const long one_grid = units + static_cast<long>(nseg) * a.b;
+  if (units >= kOneLaunchMinRowStatUnits && per1 == 16 && per == 4 && one_grid <= kMaxRowStatUnits) {
+    // the default widths: statistics and acceptance in one launch (a grid as
+    // large as one statistics pass may be)
+    const dim3 g1(static_cast<unsigned>(one_grid));
     const size_t dyn = static_cast<size_t>(nseg) * sizeof(double);
     if (unit)
       hipLaunchKernelGGL((accept_logits_kernel<16, true, 4>), g1, block, dyn, stream, a, units, nseg);

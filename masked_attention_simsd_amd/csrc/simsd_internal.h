@@ -203,6 +203,8 @@ hipError_t launch_commit_kv(const CommitArgs& a, hipStream_t stream);
 // in logits mode (same stream)
 hipError_t launch_accept_logits(const AcceptArgs& a, hipStream_t stream);
 constexpr int kRowStatSeg = 4096;  // smallest statistics segment (sizes the workspace)
-constexpr long kMaxRowStatUnits = 1L << 24;  // rows x segments of one statistics pass
+// rows x segments of one statistics pass: its grid of 256-thread workgroups
+// must stay below 2^32 work-items, the dispatch's limit per dimension
+constexpr long kMaxRowStatUnits = (1L << 24) - 1;
 
 }  // namespace simsd

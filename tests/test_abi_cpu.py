@@ -236,6 +236,10 @@ def test_accept_logits_host_errors(lib):
     n = lib.simsd_accept_logits_workspace(8, 16, 151936)
     assert n > lib.simsd_accept_workspace(8, 16, 151936) and n % 256 == 0
     assert lib.simsd_accept_logits_workspace(65536, 64, 1 << 21) == 0  # statistics units over 2^24
+    # a statistics grid of 2^24 workgroups of 256 threads would be 2^32
+    # work-items, one past a dispatch's limit: refused; one segment less fits
+    assert lib.simsd_accept_logits_workspace(4096, 64, 32 * 4096) == 0
+    assert lib.simsd_accept_logits_workspace(4096, 64, 31 * 4096) > 0
 
 
 def test_attention_mask_host_errors(lib):
