@@ -6,7 +6,8 @@ bf16 Q/K/V, vocab 32768), all launched on one stream with inputs resident in
 HBM. The form with RoPE-copy fused into the attention launch
 (simsd_verify_attention_rope, which also writes the rotated block keys) is
 timed beside it. At least ceil(1 GB / prefix KV bytes) input sets are rotated so the
-prefix KV of a step is not served from the 256 MB MALL.
+prefix KV of a step is not served from the 256 MB MALL; the accept-from-logits
+launches rotate over at least 640 MB of logits copies for the same reason.
 
 Order of work: one step on fresh inputs (kept for the parity check); about
 20 ms of untimed steps (the clocks come up); each entry point alone, 100
@@ -51,6 +52,8 @@ METRIC = "verified blocks/s + achieved HBM GB/s & MFMA % (B=8, 4K prefix, bf16)"
 ATTN_SOURCES = ("masked_attention_simsd_amd/csrc/verify_attention.hip",
                 "masked_attention_simsd_amd/csrc/simsd_internal.h")
 MALL_EVICT_BYTES = 1 << 30  # rotate at least this much prefix KV per pass over the sets
+# and at least this much target + draft logits over the accept-from-logits launches
+LOGITS_EVICT_BYTES = 640 << 20
 
 
 def counter_file(workload):
@@ -307,6 +310,24 @@ def main():
                       P(s["tau"]), P(s["u"]), b, B, w.V, P(Ls[j]), P(Cs[j]), None, P(ws_accl),
                       ws_accl.numel(), hs)
         calls.append((rope, attn, acc, fused, acc_logits))
+    # The accept-from-logits launches rotate over at least LOGITS_EVICT_BYTES of
+    # logits (the sets alone hold about 268 MB of them on b8 and ragged, of
+    # which the 256 MB MALL keeps part from one pass to the next): extra
+    # copies of the logits, the other inputs shared with the sets.
+    lg_bytes = 2 * b * B * w.V * 4
+    n_lg = max(len(sets), -(-LOGITS_EVICT_BYTES // lg_bytes))
+    lg_copies = []
+    calls_logits = []
+    for j in range(n_lg):
+        jj = j % len(sets)
+        if j < len(sets):
+            calls_logits.append((calls[j][4],))
+            continue
+        s = sets[jj]
+        zt, zd = s["target_logits"].clone(), s["draft_logits"].clone()
+        lg_copies.append((zt, zd))
+        calls_logits.append(((P(zt), P(zd), ctypes.c_float(1.0), P(s["draft"]), P(s["tau"]), P(s["u"]), b, B,
+                              w.V, P(Ls[jj]), P(Cs[jj]), None, P(ws_accl), ws_accl.numel(), hs),))
 
     def step(i):
         rope, attn, acc = calls[i % len(calls)][:3]
@@ -400,7 +421,7 @@ def main():
                "rope_copy": (lib.simsd_rope_copy, calls, 0),
                "accept": (lib.simsd_accept, calls, 2),
                "verify_attention_rope": (lib.simsd_verify_attention_rope, calls, 3),
-               "accept_logits": (lib.simsd_accept_logits, calls, 4),
+               "accept_logits": (lib.simsd_accept_logits, calls_logits, 0),
                "commit_kv": (lib.simsd_commit_kv, calls_commit, 0)}
     # Untimed steps for about 20 ms first: from idle the chip runs slow until
     # its clocks come up (single attention launches measured 60-72 us on b8
