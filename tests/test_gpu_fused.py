@@ -54,6 +54,13 @@ CASES = [
     (1, 8, 8, 128, 1, (0, 0), 0, 0),
     (1, 4, 1, 64, 64, (130, 130), binding.SIMSD_ROPE_NO_COPY, binding.SIMSD_OUT_F32),
     (1, 32, 8, 128, 64, (300, 300), 0, binding.SIMSD_KV_HEAD_MAJOR),
+    # 64-row workgroups whose 64-position table does not fit beside the 64 x 3
+    # ring: the fused launch takes 64 x 2, the two-launch reference 64 x 3 (the
+    # ring's depth changes no arithmetic), and one whose 48 positions fit
+    (1, 8, 8, 128, 32, (300, 300), binding.SIMSD_ROPE_NO_COPY, 0),
+    (2, 16, 16, 128, 32, (600, 2000), binding.SIMSD_ROPE_NO_COPY,
+     binding.SIMSD_KV_HEAD_MAJOR | binding.SIMSD_OUT_F32),
+    (2, 8, 8, 128, 24, (500, 1800), binding.SIMSD_ROPE_NO_COPY, 0),
     (1, 8, 2, 128, 32, (500, 500), binding.SIMSD_ROPE_NO_COPY, 0),
     # a position per pair (a later round of a block)
     (3, 8, 2, 128, 8, (100, 700), binding.SIMSD_ROPE_POSITIONS, 0),
