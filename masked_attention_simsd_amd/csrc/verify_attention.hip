@@ -619,7 +619,10 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
           }
       }
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb) {
+        // this tile's bits at fixed positions, then one shift into place (a
+        // per-key variable 64-bit shift compiled into a chain of branches)
+        uint32_t w = 0;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -630,8 +633,10 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
               ok = c < twoB && (((c >= 64 ? mhi[qb] : mlo[qb]) >> (c & 63)) & 1ull) != 0;
             else
               ok = c < twoB && block_allowed(slot_q[qb], tau_q[qb], c >= B, tau_k[kb][i], a.data_rule);
-            if (ok) blk_bits[qb] |= 1ull << (bt * NKB * 4 + kb * 4 + i);
+            w |= ok ? (1u << (kb * 4 + i)) : 0u;
           }
+        blk_bits[qb] |= static_cast<uint64_t>(w) << ((bt * NKB * 4) & 63);
+      }
     }
   }
 
@@ -691,14 +696,22 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (need_mask) {
+        // Branch-free inside: this tile's block bits in one word (block
+        // tiles) or the valid-key bound (a partial prefix tile), then a
+        // select per key. Its inputs pass through an empty volatile asm so
+        // that none of this work is hoisted above the branch onto every
+        // full tile (hoisted compares cost b16 about 4 us).
+        uint32_t bw = static_cast<uint32_t>(blk_bits[qb] >> ((t * NKB * 4) & 63));
+        int lim = nvalid - (kw0 + 8 * a16);  // this lane's keys at offsets below lim are valid
+        int isblk = blk ? 1 : 0;
+        asm volatile("" : "+v"(bw), "+v"(lim), "+v"(isblk));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kl = kw0 + 32 * (kb >> 1) + 8 * a16 + 4 * (kb & 1) + i;
-            const bool ok = blk ? ((blk_bits[qb] >> (t * NKB * 4 + kb * 4 + i)) & 1ull) != 0
-                                : kl < nvalid;
-            if (!ok) sacc[qb][kb][i] = -INFINITY;
+            const int off = 32 * (kb >> 1) + 4 * (kb & 1) + i;
+            const bool ok = isblk ? ((bw >> (kb * 4 + i)) & 1u) != 0u : off < lim;
+            sacc[qb][kb][i] = ok ? sacc[qb][kb][i] : -INFINITY;
           }
       }
       float mx = sacc[qb][0][0];
