@@ -821,47 +821,47 @@ __global__ __launch_bounds__(NW * 64) void verify_attn_kernel(AttnArgs a) {
     SIMSD_LDS uint8_t* const kst_p = ring_l + (t % NS) * STAGE_B;
     const bool write = a.k_rot != nullptr && split == 0 && slice == 0;
     constexpr int HALF_CH = CH / 2;
-    const int per_row = a.rope_interleaved ? CH : HALF_CH;
-    for (int it = tid; it < TK * per_row; it += NW * 64) {
-      const int row = it / per_row, cc = it % per_row;
+    // items of 8 bytes (half a 16-byte chunk: 4 pairs of the split halves, 2
+    // of the interleaved form), over the tile's valid rows only, so that
+    // every thread of a b8 workgroup takes one (with 16-byte items over all
+    // rows, half of them had nothing to do and the others eight rotations)
+    const int per_row = 2 * (a.rope_interleaved ? CH : HALF_CH);
+    const int nrow = min(TK, twoB - r0);
+    for (int it = tid; it < nrow * per_row; it += NW * 64) {
+      const int row = it / per_row, cc = (it % per_row) >> 1, hf = it & 1;
       const int c = r0 + row;
-      if (c >= twoB) continue;
       const int sw = swz_k<D>(row);
       const double* tr = rope_tab + static_cast<size_t>(rope_pos_row(c, B, a.rope_no_copy)) * rope_row_doubles<D>();
       union U {
-        u32x4 u;
-        uint16_t h[8];
+        u32x2 u;
+        uint16_t h[4];
       };
-      SIMSD_LDS u32x4* pa = reinterpret_cast<SIMSD_LDS u32x4*>(kst_p + row * ROW_B + 16 * (cc ^ sw));
+      SIMSD_LDS u32x2* pa = reinterpret_cast<SIMSD_LDS u32x2*>(kst_p + row * ROW_B + 16 * (cc ^ sw) + 8 * hf);
+      uint16_t* const dst = write ? a.k_rot + ((static_cast<size_t>(s) * twoB + c) * a.Hkv + g) * D : nullptr;
       U x;
       x.u = *pa;
       if (a.rope_interleaved) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int i = (8 * cc + j) / 2;
+        for (int j = 0; j < 4; j += 2) {
+          const int i = (8 * cc + 4 * hf + j) / 2;
           rope_rotate(x.h[j], x.h[j + 1], tr[2 * i], tr[2 * i + 1], &x.h[j], &x.h[j + 1]);
         }
         *pa = x.u;
       } else {
-        SIMSD_LDS u32x4* pb = reinterpret_cast<SIMSD_LDS u32x4*>(kst_p + row * ROW_B + 16 * ((cc + HALF_CH) ^ sw));
+        SIMSD_LDS u32x2* pb =
+            reinterpret_cast<SIMSD_LDS u32x2*>(kst_p + row * ROW_B + 16 * ((cc + HALF_CH) ^ sw) + 8 * hf);
         U y;
         y.u = *pb;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * cc + j;
+        for (int j = 0; j < 4; ++j) {
+          const int i = 8 * cc + 4 * hf + j;
           rope_rotate(x.h[j], y.h[j], tr[2 * i], tr[2 * i + 1], &x.h[j], &y.h[j]);
         }
         *pa = x.u;
         *pb = y.u;
-        if (write) {
-          uint16_t* dst = a.k_rot + ((static_cast<size_t>(s) * twoB + c) * a.Hkv + g) * D;
-          *reinterpret_cast<u32x4*>(dst + 8 * (cc + HALF_CH)) = y.u;
-        }
+        if (write) *reinterpret_cast<u32x2*>(dst + 8 * (cc + HALF_CH) + 4 * hf) = y.u;
       }
-      if (write) {
-        uint16_t* dst = a.k_rot + ((static_cast<size_t>(s) * twoB + c) * a.Hkv + g) * D;
-        *reinterpret_cast<u32x4*>(dst + 8 * cc) = x.u;
-      }
+      if (write) *reinterpret_cast<u32x2*>(dst + 8 * cc + 4 * hf) = x.u;
     }
     wait_lgkm0();
     block_barrier();  // rotated rows visible to every wave
